@@ -1,0 +1,126 @@
+"""Pins for the event semantics and the scheduler simulator (CPU only)."""
+
+import os
+import random
+
+import pytest
+
+from oracle import events as ev
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _steps(name):
+    out = []
+    for line in open(os.path.join(GOLD, name), encoding="utf-8"):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            out.append(tuple(line.split()))
+    return out
+
+
+def _walk_graph():
+    return ev.TaskGraph(
+        tasks=["gemm0", "gemm1", "gemm2", "rs"],
+        waits={"rs": ["E"]},
+        notifies={"gemm0": ["E"], "gemm1": ["E"]},
+        wait_count={"E": 2},
+    )
+
+
+def _dur(t):
+    return {"gemm0": 1.0, "gemm1": 2.0, "gemm2": 5.0, "rs": 1.0}[t]
+
+
+def _match(trace, expected):
+    """Every expected step appears in the trace, in order."""
+    it = iter(trace)
+    for exp in expected:
+        for step in it:
+            act = step[0]
+            if act != exp[0]:
+                continue
+            if act in ("notify", "spin"):
+                ok = (str(step[1]) == exp[1] and step[2] == exp[2] and str(step[4]) == exp[3])
+            elif act in ("run", "push"):
+                ok = (exp[1] == "*" or str(step[1]) == exp[1]) and step[2] == exp[2]
+            else:
+                ok = False
+            if ok:
+                break
+        else:
+            return False
+    return True
+
+
+def test_static_walkthrough():
+    g = _walk_graph()
+    g.tasks.remove("gemm2")
+    trace, cnt, runs = ev.run_static(g, [["gemm0", "rs"], ["gemm1"]], _dur)
+    assert _match(trace, _steps("static_walkthrough.txt")), trace
+    assert cnt["E"] == 0 and all(v == 1 for v in runs.values())
+
+
+def test_dynamic_walkthrough():
+    g = _walk_graph()
+    trace, cnt, runs = ev.run_dynamic(g, 2, ["gemm0", "gemm1", "gemm2"], _dur)
+    assert _match(trace, _steps("dynamic_walkthrough.txt")), trace
+    # the producer never waits: no spin steps exist in dynamic mode
+    assert not any(s[0] == "spin" for s in trace)
+    assert cnt["E"] == 0 and all(v == 1 for v in runs.values())
+    # exactly one push of the consumer, by the notifier that zeroed the counter
+    pushes = [s for s in trace if s[0] == "push"]
+    assert pushes == [("push", 1, "rs")]
+
+
+def _random_layered(seed, layers=4, width=6):
+    rnd = random.Random(seed)
+    tasks, waits, notifies, wc = [], {}, {}, {}
+    prev = []
+    for L in range(layers):
+        cur = ["t%d_%d" % (L, i) for i in range(rnd.randint(1, width))]
+        for t in cur:
+            tasks.append(t)
+            if prev:
+                e = "e_" + t
+                producers = rnd.sample(prev, rnd.randint(1, len(prev)))
+                for p in producers:
+                    notifies.setdefault(p, []).append(e)
+                waits[t] = [e]
+                wc[e] = len(producers)
+        prev = cur
+    return ev.TaskGraph(tasks, waits, notifies, wc)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_graphs_exactly_once(seed):
+    g = _random_layered(seed)
+    rnd = random.Random(100 + seed)
+    dur = lambda t: 1.0 + (hash((seed, t)) % 7)
+    # static: round-robin over workers, each list in topological (layer) order
+    nw = rnd.randint(1, 4)
+    lists = [g.tasks[w::nw] for w in range(nw)]
+    _, cnt, runs = ev.run_static(g, lists, dur)
+    assert all(v == 0 for v in cnt.values()) and all(v == 1 for v in runs.values())
+    # dynamic, fetch 1 and 4
+    init = [t for t in g.tasks if not g.waits[t]]
+    for fetch in (1, 4):
+        _, cnt, runs = ev.run_dynamic(g, nw, init, dur, fetch=fetch)
+        assert all(v == 0 for v in cnt.values()) and all(v == 1 for v in runs.values())
+
+
+def test_wrong_wait_count_is_detected():
+    g = _walk_graph()
+    g.tasks.remove("gemm2")
+    g.wait_count["E"] = 3      # one notify too few will ever arrive
+    with pytest.raises(ev.Deadlock):
+        ev.run_static(g, [["gemm0", "rs"], ["gemm1"]], _dur)
+    _, cnt, runs = ev.run_dynamic(g, 2, ["gemm0", "gemm1"], _dur)
+    assert cnt["E"] == 1 and runs["rs"] == 0     # consumer never pushed
+
+
+def test_list_out_of_topological_order_deadlocks():
+    g = _walk_graph()
+    g.tasks.remove("gemm2")
+    with pytest.raises(ev.Deadlock):
+        ev.run_static(g, [["rs", "gemm0", "gemm1"]], _dur)
