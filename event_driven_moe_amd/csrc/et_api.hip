@@ -1,0 +1,271 @@
+// et_api.hip -- the C ABI: workspace planning, argument validation and launch.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "../../include/et.h"
+#include "et_device.hpp"
+#include "et_launch.hpp"
+#include "et_plan.hpp"
+
+namespace et {
+
+RunArgs LaunchCommon::run_args() const {
+  RunArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.hdr = reinterpret_cast<int*>(ws);
+  a.counters = reinterpret_cast<int*>(ws + plan->off_counters);
+  a.n_events = plan->n_events;
+  a.slots = reinterpret_cast<int*>(ws + plan->off_slots);
+  a.q_cap = plan->max_tasks;
+  a.runs = (debug & ET_DEBUG_COUNTS) ? reinterpret_cast<int*>(ws + plan->off_runs) : nullptr;
+  a.sched = sched;
+  a.fetch = fetch;
+  a.phase = -1;
+  a.timeout = (long long)timeout_ms * 100000ll;
+  a.n_init = 0;
+  a.total_hint = kUnknownTotal;
+  a.extent = 0;
+  return a;
+}
+
+// Clears [0, bytes) of the workspace and writes the header (no memset node,
+// so the call can also sit in a captured graph).
+__global__ void ws_init_kernel(int* ws, size_t words, int workload) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < words;
+       i += (size_t)gridDim.x * blockDim.x)
+    ws[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    ws[HDR_MAGIC] = kMagic;
+    ws[HDR_WORKLOAD] = workload;
+    ws[HDR_QTOTAL] = kUnknownTotal;
+  }
+}
+
+namespace {
+
+std::atomic<int> g_workers[64];   // cached workgroups per device (0 = not yet known)
+
+int workers_for_current_device(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ET_EHIP;
+  if (dev < 0 || dev >= 64) return ET_EHIP;
+  int g = g_workers[dev].load(std::memory_order_relaxed);
+  if (g == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return ET_EHIP;
+    if (cus <= 0) return ET_EHIP;
+    g = cus;   // one persistent workgroup per compute unit
+    g_workers[dev].store(g, std::memory_order_relaxed);
+  }
+  *out = g;
+  return ET_OK;
+}
+
+bool valid_sched(int s) { return s >= ET_SCHED_STATIC && s <= ET_SCHED_PER_OP; }
+
+int fill_common(LaunchCommon& lc, void* ws, const et_plan* plan, int sched, const et_opts* o,
+                hipStream_t stream, int workload) {
+  if (!ws || !plan) return ET_EWORKSPACE;
+  if (plan->workload != workload) return ET_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return ET_EWORKSPACE;
+  if (!valid_sched(sched)) return ET_EINVAL;
+  lc.plan = plan;
+  lc.ws = static_cast<char*>(ws);
+  lc.sched = sched;
+  lc.fetch = o && o->fetch_batch > 0 ? o->fetch_batch : 4;
+  if (lc.fetch > 8) return ET_EINVAL;
+  lc.debug = o ? o->debug_flags : 0;
+  lc.timeout_ms = o && o->timeout_ms > 0 ? o->timeout_ms : 2000;
+  lc.tile = o ? o->tile : -1;
+  if (o && (o->tile < -1 || o->tile >= TV_COUNT)) return ET_EINVAL;
+  lc.stream = stream;
+  return workers_for_current_device(&lc.G);
+}
+
+}  // namespace
+}  // namespace et
+
+using namespace et;
+
+extern "C" {
+
+int et_plan_workspace(int workload, int max_tokens, int hidden, int inter, int n_experts,
+                      int top_k, et_plan* plan) {
+  if (!plan) return ET_EINVAL;
+  std::memset(plan, 0, sizeof(*plan));
+  if (max_tokens <= 0) return ET_EINVAL;
+  plan->workload = workload;
+  plan->max_tokens = max_tokens;
+  size_t aux = 0;
+  if (workload == ET_WL_SPLITK) {
+    if (max_tokens % 32 != 0) return ET_EUNSUPPORTED;
+    if (hidden != 0 && hidden != 128) return ET_EUNSUPPORTED;
+    if (max_tokens > (1 << 24)) return ET_EUNSUPPORTED;
+    SplitKPlan p{max_tokens / 32};
+    plan->hidden = 128;
+    plan->n_events = p.n_events();
+    plan->max_tasks = p.max_tasks();
+  } else if (workload == ET_WL_MLP) {
+    if (hidden <= 0 || inter <= 0) return ET_EINVAL;
+    if (hidden % 128 || inter % 128) return ET_EUNSUPPORTED;
+    if ((size_t)inter * hidden * 2 >= (1ull << 31)) return ET_EUNSUPPORTED;
+    if ((size_t)max_tokens * (hidden > inter ? hidden : inter) * 4 >= (1ull << 31))
+      return ET_EUNSUPPORTED;
+    MlpPlan p{max_tokens, hidden, inter};
+    plan->hidden = hidden;
+    plan->inter = inter;
+    plan->n_events = p.n_events_max();
+    plan->max_tasks = p.max_tasks();
+    aux = (size_t)max_tokens * inter * 2;
+  } else if (workload == ET_WL_MOE) {
+    if (hidden <= 0 || inter <= 0 || n_experts <= 0 || top_k <= 0) return ET_EINVAL;
+    if (top_k > n_experts) return ET_EINVAL;
+    if (hidden % 128 || inter % 128) return ET_EUNSUPPORTED;
+    if (n_experts > kMaxExperts || top_k > kMaxTopK) return ET_EUNSUPPORTED;
+    const size_t tk = (size_t)max_tokens * top_k;
+    if (tk * inter * 2 >= (1ull << 31) || (size_t)max_tokens * hidden * 2 >= (1ull << 31) ||
+        (size_t)inter * hidden * 2 >= (1ull << 31) || tk * hidden * 4 >= (1ull << 34))
+      return ET_EUNSUPPORTED;
+    MoePlan p{max_tokens, hidden, inter, n_experts, top_k, moe_n_route(n_experts)};
+    if ((size_t)p.n_events_max() >= (1ull << 30) || (size_t)p.max_tasks() >= (1ull << 30))
+      return ET_EUNSUPPORTED;
+    plan->hidden = hidden;
+    plan->inter = inter;
+    plan->n_experts = n_experts;
+    plan->top_k = top_k;
+    plan->n_events = p.n_events_max();
+    plan->max_tasks = p.max_tasks();
+    aux = moe_aux_layout(p).bytes;
+  } else {
+    return ET_EINVAL;
+  }
+  size_t o = kHdrBytes;
+  plan->off_counters = o;
+  o = align_up(o + (size_t)2 * plan->n_events * 4, 256);
+  plan->off_slots = o;
+  o = align_up(o + (size_t)plan->max_tasks * 4, 256);
+  plan->off_runs = o;
+  o = align_up(o + (size_t)plan->max_tasks * 4, 256);
+  plan->off_aux = o;
+  plan->aux_bytes = aux;
+  plan->bytes = align_up(o + aux, 256);
+  return ET_OK;
+}
+
+int et_workspace_init(void* ws, const et_plan* plan, hipStream_t stream) {
+  if (!ws || !plan || plan->bytes == 0) return ET_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return ET_EWORKSPACE;
+  const size_t words = plan->off_aux / 4;   // header, counters, slots, run counts
+  hipLaunchKernelGGL(ws_init_kernel, dim3(256), dim3(256), 0, stream, static_cast<int*>(ws),
+                     words, plan->workload);
+  return hipGetLastError() == hipSuccess ? ET_OK : ET_EHIP;
+}
+
+int et_workspace_layout(const et_plan* plan, int n_tokens, et_layout* out) {
+  if (!plan || !out) return ET_EINVAL;
+  std::memset(out, 0, sizeof(*out));
+  out->counters_bank[0] = plan->off_counters;
+  out->counters_bank[1] = plan->off_counters + (size_t)plan->n_events * 4;
+  out->n_events = plan->n_events;
+  out->runs = plan->off_runs;
+  if (plan->workload == ET_WL_MLP) {
+    out->h = plan->off_aux;
+  } else if (plan->workload == ET_WL_MOE) {
+    MoePlan p{plan->max_tokens, plan->hidden, plan->inter, plan->n_experts, plan->top_k,
+              moe_n_route(plan->n_experts)};
+    const MoeAux a = moe_aux_layout(p);
+    const size_t b = plan->off_aux;
+    out->topk_ids = b + a.topk_ids;
+    out->topk_w = b + a.topk_w;
+    out->counts = b + a.counts;
+    out->tok_indptr = b + a.tok_indptr;
+    out->perm = b + a.perm;
+    out->inv = b + a.inv;
+    out->task_indptr = b + a.task_indptr;
+    out->h = b + a.h;
+  }
+  (void)n_tokens;
+  return ET_OK;
+}
+
+int et_splitk_reduce(const float* A, int rows, float* Bpart, float* C, void* ws,
+                     const et_plan* plan, int sched, const et_opts* opts, hipStream_t stream) {
+  LaunchCommon lc;
+  int e = fill_common(lc, ws, plan, sched, opts, stream, ET_WL_SPLITK);
+  if (e) return e;
+  if (rows < 0 || rows % 32 != 0) return ET_EUNSUPPORTED;
+  if (rows > plan->max_tokens) return ET_EWORKSPACE;
+  if (rows == 0) return ET_OK;
+  if (!A || !Bpart || !C) return ET_EINVAL;
+  return launch_splitk(lc, A, rows, Bpart, C);
+}
+
+int et_mlp(const uint16_t* x, int n_tokens, const uint16_t* w_gate, const uint16_t* w_up,
+           const uint16_t* w_down, float* y, void* ws, const et_plan* plan, int sched,
+           const et_opts* opts, hipStream_t stream) {
+  LaunchCommon lc;
+  int e = fill_common(lc, ws, plan, sched, opts, stream, ET_WL_MLP);
+  if (e) return e;
+  if (n_tokens < 0) return ET_EINVAL;
+  if (n_tokens > plan->max_tokens) return ET_EWORKSPACE;
+  if (n_tokens == 0) return ET_OK;
+  if (!x || !w_gate || !w_up || !w_down || !y) return ET_EINVAL;
+  return launch_mlp(lc, x, n_tokens, w_gate, w_up, w_down, y);
+}
+
+int et_moe_layer(const float* logits, const uint16_t* x, int n_tokens, const uint16_t* w_gate,
+                 const uint16_t* w_up, const uint16_t* w_down, float* out, void* ws,
+                 const et_plan* plan, int sched, const et_opts* opts, hipStream_t stream) {
+  LaunchCommon lc;
+  int e = fill_common(lc, ws, plan, sched, opts, stream, ET_WL_MOE);
+  if (e) return e;
+  if (n_tokens < 0) return ET_EINVAL;
+  if (n_tokens > plan->max_tokens) return ET_EWORKSPACE;
+  if (n_tokens == 0) return ET_OK;
+  if (!logits || !x || !w_gate || !w_up || !w_down || !out) return ET_EINVAL;
+  return launch_moe(lc, logits, x, n_tokens, w_gate, w_up, w_down, out);
+}
+
+int et_read_status(const void* ws, const et_plan* plan, hipStream_t stream, et_report* out) {
+  if (!ws || !plan || !out) return ET_EINVAL;
+  if (hipStreamSynchronize(stream) != hipSuccess) return ET_EHIP;
+  int h[HDR_WORDS];
+  if (hipMemcpy(h, ws, sizeof(h), hipMemcpyDeviceToHost) != hipSuccess) return ET_EHIP;
+  std::memset(out, 0, sizeof(*out));
+  if (h[HDR_MAGIC] != kMagic) return ET_EWORKSPACE;
+  out->status = h[HDR_ERR];
+  out->err_info[0] = h[HDR_ERR_A];
+  out->err_info[1] = h[HDR_ERR_B];
+  out->err_info[2] = h[HDR_ERR_C];
+  out->bank = h[HDR_BANK];
+  out->calls = h[HDR_CALLS];
+  out->last_tasks = h[HDR_LAST_TASKS];
+  out->q_head = h[HDR_QHEAD];
+  out->q_push = h[HDR_QPUSH];
+  out->last_extent = h[HDR_EXT0 + (1 - (h[HDR_BANK] & 1))];
+  return ET_OK;
+}
+
+const char* et_status_str(int s) {
+  switch (s) {
+    case ET_OK: return "ok";
+    case ET_EINVAL: return "invalid argument";
+    case ET_EWORKSPACE: return "workspace missing, too small or planned for other dimensions";
+    case ET_EHIP: return "HIP runtime error";
+    case ET_ETIMEOUT: return "device wait exceeded the watchdog";
+    case ET_EUNSUPPORTED: return "unsupported dimensions";
+    case ET_ESTATE: return "event over-notified or ready queue overflow";
+    default: return "unknown status";
+  }
+}
+
+int et_num_workers(void) {
+  int g = 0;
+  int e = workers_for_current_device(&g);
+  return e ? -e : g;
+}
+
+}  // extern "C"

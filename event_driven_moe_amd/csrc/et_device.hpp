@@ -1,0 +1,348 @@
+// et_device.hpp -- device side of the Event Tensor runtime for gfx950.
+//
+// Event Tensors (Event Tensor notes = page "Event Tensor：用“事件张量”编译动态
+// Megakernel", notes.kuangjux.top, sections "Event Tensor 抽象" and "Minimal
+// runtime") lower to plain int32 arrays: notify() is an atomic decrement,
+// wait() holds until the count is zero, and under dynamic scheduling the
+// notify that zeroes a count pushes the event's consumers to a ready queue
+// (section "动态调度").  The only mutable run-time state is the counters and
+// the queue.
+//
+// Storage choice: a counter is stored RELATIVE to its wait count, i.e. the
+// stored value is (count - wait_count).  Every event is therefore armed by the
+// same value, 0, whatever its wait count, which may depend on the run-time
+// token count (symbolic event shapes) or on routing results (data-dependent
+// counts); the wait count is supplied by whoever waits or notifies, and an
+// event has fired when its stored value equals -wait_count.  Counters live in
+// two banks: a call uses one bank and, in its prologue, re-arms (zeroes) the
+// part of the other bank that the previous call used; the last workgroup to
+// leave flips the bank.  No host memset and no grid barrier are needed.
+//
+// Memory ordering: producers and consumers run on different compute units,
+// often on different XCDs with separate L2 caches.  notify() makes every wave
+// of the producer perform an agent-scope release before the workgroup barrier
+// and the decrement; wait() and queue pops end with an agent-scope acquire.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/et.h"
+#include "et_plan.hpp"
+
+namespace et {
+
+// ---------------------------------------------------------------------------
+// atomics and fences (agent scope = the whole GPU)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ long long now_ticks() {
+  return (long long)__builtin_amdgcn_s_memrealtime();   // constant 100 MHz clock
+}
+__device__ __forceinline__ int ld_rlx(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_rlx(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_rel(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int add_rlx(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int add_rel(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int add_acqrel(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// ---------------------------------------------------------------------------
+// per-call arguments and context
+// ---------------------------------------------------------------------------
+struct RunArgs {
+  int* hdr;            // workspace header words (HDR_*)
+  int* counters;       // bank 0; bank 1 starts n_events later
+  int n_events;
+  int* slots;          // ready-queue slots (pushed tasks; implicit initial tasks need none)
+  int q_cap;
+  int* runs;           // per-task run counts, or nullptr
+  int sched;           // ET_SCHED_*
+  int fetch;           // dynamic: slots claimed per atomic
+  int phase;           // per-op mode: operator this launch runs
+  long long timeout;   // watchdog, 100 MHz ticks
+  int n_init;          // dynamic: tasks [0, n_init) are in the queue from the start
+  int total_hint;      // dynamic: total tasks when known at launch, else kUnknownTotal
+  int extent;          // counters this call uses (a prefix of its bank)
+};
+
+// Workgroup-shared scratch for broadcasts.
+struct Shared {
+  int v[8];
+};
+
+struct Ctx {
+  RunArgs a;
+  int* ev;             // this call's bank
+  int wg, G;
+  Shared* sh;
+};
+
+__device__ __forceinline__ void raise_fault(const RunArgs& a, int code, int x, int y, int v) {
+  int expected = 0;
+  if (__hip_atomic_compare_exchange_strong(&a.hdr[HDR_ERR], &expected, code, __ATOMIC_RELAXED,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+    st_rlx(&a.hdr[HDR_ERR_A], x);
+    st_rlx(&a.hdr[HDR_ERR_B], y);
+    st_rlx(&a.hdr[HDR_ERR_C], v);
+  }
+}
+
+__device__ __forceinline__ bool faulted(const RunArgs& a) { return ld_rlx(&a.hdr[HDR_ERR]) != 0; }
+
+// Thread 0's value to the whole workgroup (two barriers so the slot can be reused).
+__device__ __forceinline__ int wg_bcast(const Ctx& c, int v, int slot = 0) {
+  if (threadIdx.x == 0) c.sh->v[slot] = v;
+  __syncthreads();
+  int r = c.sh->v[slot];
+  __syncthreads();
+  return r;
+}
+
+// Spin (thread 0 only) until counter `idx` of this call's bank reaches
+// -wait_count.  Returns 1, or 0 after a fault (own or another workgroup's).
+__device__ __noinline__ int spin_until(const Ctx& c, int idx, int wait_count, int task) {
+  const int* p = c.ev + idx;
+  const int target = -wait_count;
+  int v = ld_rlx(p);
+  if (v == target) return 1;
+  long long t0 = now_ticks();
+  for (int it = 1;; ++it) {
+    if (v < target) {
+      raise_fault(c.a, ET_ESTATE, task, idx, v);
+      return 0;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    v = ld_rlx(p);
+    if (v == target) return 1;
+    if ((it & 63) == 0) {
+      if (faulted(c.a)) return 0;
+      if (now_ticks() - t0 > c.a.timeout) {
+        raise_fault(c.a, ET_ETIMEOUT, task, idx, v);
+        return 0;
+      }
+    }
+  }
+}
+
+// wait(): the whole workgroup holds until event `idx` has received
+// `wait_count` notifies.  Returns false when the call is being abandoned.
+__device__ __forceinline__ bool wg_wait(const Ctx& c, int idx, int wait_count, int task) {
+  int ok = 1;
+  if (threadIdx.x == 0) {
+    ok = spin_until(c, idx, wait_count, task);
+    fence_acquire();
+  }
+  return wg_bcast(c, ok, 1) != 0;
+}
+
+// Several events at once (all must fire).
+__device__ __forceinline__ bool wg_wait_range(const Ctx& c, int first, int n, int wait_count,
+                                              int task) {
+  int ok = 1;
+  if (threadIdx.x == 0) {
+    for (int i = 0; i < n && ok; ++i) ok = spin_until(c, first + i, wait_count, task);
+    fence_acquire();
+  }
+  return wg_bcast(c, ok, 1) != 0;
+}
+
+// Publish this workgroup's global stores at agent scope (every wave), then
+// synchronise the workgroup.  Precedes every notify.
+__device__ __forceinline__ void wg_release() {
+  fence_release();
+  __syncthreads();
+}
+
+// notify(): decrement event `idx` by n.  Must follow wg_release().  Returns
+// (to every thread) whether this notify fired the event.  With `acquire`, the
+// firing workgroup also acquires what the other notifiers published (needed
+// when it goes on to push or run the consumers).
+__device__ __forceinline__ bool wg_notify(const Ctx& c, int idx, int n, int wait_count, int task,
+                                          bool acquire) {
+  int fired = 0;
+  if (threadIdx.x == 0) {
+    int* p = c.ev + idx;
+    int old = acquire ? add_acqrel(p, -n) : add_rel(p, -n);
+    int now = old - n;
+    if (now < -wait_count) raise_fault(c.a, ET_ESTATE, task, idx, now);
+    fired = now == -wait_count;
+  }
+  return wg_bcast(c, fired, 2) != 0;
+}
+
+// Thread-0-only notify (no broadcast), for fire-and-forget notifies after wg_release().
+__device__ __forceinline__ void t0_notify(const Ctx& c, int idx, int n, int wait_count, int task) {
+  if (threadIdx.x == 0) {
+    int old = add_rel(c.ev + idx, -n);
+    if (old - n < -wait_count) raise_fault(c.a, ET_ESTATE, task, idx, old - n);
+  }
+}
+
+// push(): append tasks id_of(0..n-1) to the ready queue.  Whole workgroup.
+template <class F>
+__device__ __forceinline__ void wg_push(const Ctx& c, int n, F id_of) {
+  if (n <= 0) return;
+  int base = 0;
+  if (threadIdx.x == 0) base = add_rlx(&c.a.hdr[HDR_QPUSH], n);
+  base = wg_bcast(c, base, 3);
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    int s = base + i;
+    if (s < c.a.q_cap)
+      st_rel(&c.a.slots[s], id_of(i) + 1);
+    else
+      raise_fault(c.a, ET_ESTATE, -1, s, c.a.q_cap);
+  }
+}
+
+// Set the total number of tasks of this call (dynamic mode), once known.
+__device__ __forceinline__ void set_total(const Ctx& c, int total) {
+  if (threadIdx.x == 0) st_rlx(&c.a.hdr[HDR_QTOTAL], total);
+}
+
+// Worker-side claim state (meaningful in thread 0 only).
+struct PopState {
+  int base = 0;
+  int left = 0;
+};
+
+// Thread 0: slot index -> task id, -1 when the call has no more tasks,
+// -2 on a fault.
+__device__ __noinline__ int resolve_slot(const Ctx& c, int idx) {
+  if (idx < c.a.n_init) return idx;
+  const int s = idx - c.a.n_init;
+  long long t0 = 0;
+  for (int it = 0;; ++it) {
+    int total = ld_rlx(&c.a.hdr[HDR_QTOTAL]);
+    if (c.a.total_hint < total) total = c.a.total_hint;
+    if (idx >= total) return -1;
+    if (s < c.a.q_cap) {
+      int v = ld_rlx(&c.a.slots[s]);
+      if (v != 0) {
+        st_rlx(&c.a.slots[s], 0);   // leave the slot empty for the next call
+        fence_acquire();
+        return v - 1;
+      }
+    }
+    if (it == 0) t0 = now_ticks();
+    __builtin_amdgcn_s_sleep(1);
+    if ((it & 63) == 63) {
+      if (faulted(c.a)) return -2;
+      if (now_ticks() - t0 > c.a.timeout) {
+        raise_fault(c.a, ET_ETIMEOUT, -1, idx, total);
+        return -2;
+      }
+    }
+  }
+}
+
+// pop(): next task of this worker (whole workgroup); claims `fetch` slots
+// per atomic and runs them in slot order (batched fetch, Weave MoE article
+// section 2.2).
+__device__ __forceinline__ int wg_pop(const Ctx& c, PopState& ps) {
+  int t = -1;
+  if (threadIdx.x == 0) {
+    if (ps.left == 0) {
+      ps.base = add_rlx(&c.a.hdr[HDR_QHEAD], c.a.fetch);
+      ps.left = c.a.fetch;
+    }
+    int idx = ps.base + (c.a.fetch - ps.left);
+    --ps.left;
+    t = resolve_slot(c, idx);
+  }
+  return wg_bcast(c, t, 4);
+}
+
+__device__ __forceinline__ void count_run(const Ctx& c, int task) {
+  if (c.a.runs && threadIdx.x == 0) atomicAdd(&c.a.runs[task], 1);
+}
+
+// Prologue: pick this call's bank and re-arm the part of the other bank the
+// previous call used.  Returns false when the workspace carries a fault.
+__device__ __forceinline__ bool prologue(Ctx& c, const RunArgs& a, Shared* sh) {
+  c.a = a;
+  c.sh = sh;
+  c.wg = blockIdx.x;
+  c.G = gridDim.x;
+  if (ld_rlx(&a.hdr[HDR_ERR]) != 0) return false;
+  int bank = ld_rlx(&a.hdr[HDR_BANK]) & 1;
+  c.ev = a.counters + (size_t)bank * a.n_events;
+  if (a.sched != ET_SCHED_PER_OP) {
+    int* other = a.counters + (size_t)(1 - bank) * a.n_events;
+    int ext = ld_rlx(&a.hdr[HDR_EXT0 + (1 - bank)]);
+    if (ext > a.n_events) ext = a.n_events;
+    for (int i = c.wg * kThreads + threadIdx.x; i < ext; i += c.G * kThreads) other[i] = 0;
+  }
+  return true;
+}
+
+// Epilogue: the last workgroup out resets the queue, records the extent of
+// the bank it used and flips the bank for the next call.
+__device__ __forceinline__ void epilogue(const Ctx& c, int tasks_this_call) {
+  if (c.a.sched == ET_SCHED_PER_OP) return;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    fence_release();
+    int old = add_acqrel(&c.a.hdr[HDR_EXIT], 1);
+    if (old == c.G - 1) {
+      int* h = c.a.hdr;
+      int bank = ld_rlx(&h[HDR_BANK]) & 1;
+      st_rlx(&h[HDR_EXIT], 0);
+      st_rlx(&h[HDR_QHEAD], 0);
+      st_rlx(&h[HDR_QPUSH], 0);
+      st_rlx(&h[HDR_QTOTAL], kUnknownTotal);
+      st_rlx(&h[HDR_EXT0 + bank], c.a.extent);
+      st_rlx(&h[HDR_LAST_TASKS], tasks_this_call);
+      st_rlx(&h[HDR_CALLS], ld_rlx(&h[HDR_CALLS]) + 1);
+      st_rlx(&h[HDR_BANK], 1 - bank);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// buffer resources (out-of-range loads return zeros) and MFMA helpers
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr uint32_t kOOB = 0x80000000u;   // offset that is always out of range
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* p, uint32_t bytes) {
+  // word 3 = 0x00020000: raw (untyped) 32-bit data format on gfx9-family parts
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ i32x4 ld16(Rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16(i32x4 a, i32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);   // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);                                             // nearest-even
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+}  // namespace et

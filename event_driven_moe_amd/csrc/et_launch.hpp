@@ -1,0 +1,54 @@
+// et_launch.hpp -- host-side launch helpers shared by the workloads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/et.h"
+#include "et_plan.hpp"
+
+namespace et {
+
+struct RunArgs;
+
+struct LaunchCommon {
+  const et_plan* plan;
+  char* ws;
+  int sched;
+  int fetch;
+  int debug;
+  int timeout_ms;
+  int tile;
+  int G;               // workgroups of a persistent launch (one per CU)
+  hipStream_t stream;
+
+  RunArgs run_args() const;
+
+  // Launches kernel(ra, args).  Persistent launches are cooperative: every
+  // workgroup must be resident, since tasks spin on each other's events.
+  template <class A>
+  int launch(const void* kernel, RunArgs* ra, A* args, bool cooperative) const {
+    void* kargs[] = {ra, args};
+    hipError_t e;
+    if (cooperative)
+      e = hipLaunchCooperativeKernel(kernel, dim3(G), dim3(kThreads), kargs, 0, stream);
+    else
+      e = hipLaunchKernel(kernel, dim3(G), dim3(kThreads), kargs, 0, stream);
+    return e == hipSuccess ? ET_OK : ET_EHIP;
+  }
+};
+
+int launch_splitk(const LaunchCommon& lc, const float* A, int rows, float* B, float* C);
+int launch_mlp(const LaunchCommon& lc, const uint16_t* x, int B, const uint16_t* wg,
+               const uint16_t* wu, const uint16_t* wd, float* y);
+int launch_moe(const LaunchCommon& lc, const float* logits, const uint16_t* x, int T,
+               const uint16_t* wg, const uint16_t* wu, const uint16_t* wd, float* out);
+
+// Tile variant for a call (rows per tile from the token count, unless forced).
+inline int pick_tile(int tokens_per_expert_bound, int forced) {
+  if (forced >= 0 && forced < TV_COUNT) return forced;
+  if (tokens_per_expert_bound <= 16) return TV_M16;
+  if (tokens_per_expert_bound <= 32) return TV_M32;
+  return TV_M64;
+}
+
+}  // namespace et

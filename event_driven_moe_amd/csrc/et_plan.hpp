@@ -1,0 +1,172 @@
+// et_plan.hpp -- workspace layout, task-space arithmetic and tiling constants
+// shared by the host launcher and the kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+#define ET_HD __host__ __device__ __forceinline__
+
+namespace et {
+
+constexpr int kThreads = 256;      // every persistent workgroup: 4 waves of 64
+constexpr int kMagic = 0x45545431;
+
+// Workspace header: 256 int32 words.  Each word that several workgroups
+// update sits on its own 128-byte line.
+enum : int {
+  HDR_MAGIC = 0,
+  HDR_WORKLOAD = 1,
+  HDR_BANK = 32,        // bank the next call uses
+  HDR_CALLS = 33,       // completed calls
+  HDR_EXT0 = 34,        // counters of bank 0 / 1 the last call on it used
+  HDR_EXT1 = 35,
+  HDR_LAST_TASKS = 36,  // tasks run by the last call
+  HDR_ERR = 64,         // sticky fault code (0 = none)
+  HDR_ERR_A = 65,
+  HDR_ERR_B = 66,
+  HDR_ERR_C = 67,
+  HDR_QHEAD = 96,       // ready queue: slots claimed
+  HDR_QPUSH = 128,      // ready queue: slots pushed (beyond the implicit initial tasks)
+  HDR_QTOTAL = 160,     // ready queue: total tasks of this call once known (else INT_MAX)
+  HDR_EXIT = 192,       // workgroups that finished this call
+  HDR_META = 224,       // 32 words of per-call workload metadata
+  HDR_WORDS = 256
+};
+constexpr size_t kHdrBytes = HDR_WORDS * 4;
+constexpr int kUnknownTotal = 0x7fffffff;
+
+ET_HD size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+ET_HD int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// GEMM tiling.  A tile variant fixes the rows per tile (16 * MT) and the
+// columns per task of the gate/up (bn1, in h columns) and down (bn2)
+// projections.  K is consumed in blocks of 128 elements.
+// ---------------------------------------------------------------------------
+constexpr int kKBlock = 128;
+constexpr int kHTile = 128;        // MLP: one event per 128-column tile of h
+
+struct Tiling {
+  int mt;    // 16-row sub-tiles per tile
+  int bn1;   // h columns per gate/up task
+  int bn2;   // output columns per down task
+};
+
+// Variant ids (kernels are instantiated per variant).
+enum : int { TV_M16 = 0, TV_M32 = 1, TV_M64 = 2, TV_COUNT = 3 };
+
+ET_HD Tiling tiling_of(int tv) {
+  Tiling t;
+  t.mt = tv == TV_M16 ? 1 : (tv == TV_M32 ? 2 : 4);
+  t.bn1 = 16;
+  t.bn2 = 16;
+  return t;
+}
+constexpr int kMinRows = 16;       // smallest rows per tile over all variants
+constexpr int kMinCols = 16;       // smallest bn1 / bn2 over all variants
+
+// ---------------------------------------------------------------------------
+// Split-K example: rows = 32 n, 128 columns, 4 slices.
+// events: E[0..n) (wait count 4), then one "all stage-1 done" event.
+// tasks:  [0, 4n) stage-1 (i = id / 4, j = id % 4); [4n, 5n) stage-2.
+// ---------------------------------------------------------------------------
+struct SplitKPlan {
+  int n_max;
+  ET_HD int n_events() const { return n_max + 1; }
+  ET_HD int max_tasks() const { return 5 * n_max; }
+};
+
+// ---------------------------------------------------------------------------
+// Dense MLP chain.
+// events: E_h[mb][I/128] (wait count 128 / bn1), then E_gate_all.
+// tasks:  [0, n_gate) gate/up tiles (mb, n) with n fastest;
+//         [n_gate, n_gate + n_down) down tiles (mb, n2).
+// ---------------------------------------------------------------------------
+struct MlpPlan {
+  int b_max, hidden, inter;
+  ET_HD int mb(int B, const Tiling& t) const { return cdiv(B, 16 * t.mt); }
+  ET_HD int n_htiles() const { return inter / kHTile; }
+  ET_HD int n_events_max() const { return cdiv(b_max, kMinRows) * n_htiles() + 1; }
+  ET_HD int max_tasks() const {
+    return cdiv(b_max, kMinRows) * (inter / kMinCols + hidden / kMinCols);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// MoE layer.
+// Routing / grouping use n_route token chunks; chunk r covers tokens
+// [r * tpr, min((r + 1) * tpr, T)) with tpr = ceil(T / n_route).
+// events (prefix of a bank):
+//   EV_ROUTE  all routing tasks done      (wait count n_route)
+//   EV_SCAN   scan done                   (1)
+//   EV_GROUP  all grouping tasks done     (n_route)
+//   EV_G1ALL  all gate/up tasks done      (total1)        [barrier mode]
+//   EV_DOWN   all down tasks done         (total2)        [static / barrier]
+//   EV_EXP[e] rows of expert e grouped    (counts[e])     data-dependent
+//   EV_H[gb]  gate/up tiles of block gb   (inter / bn1)
+//   EV_C[t][c] down tiles covering token t, column tile c (top_k) [dynamic]
+// tasks: [0, R) routing, R scan, [R+1, 2R+1) grouping, then total1 gate/up
+//   tiles (block-major, column tile fastest), total2 down tiles, then (static,
+//   barrier, per-op) combine tiles of kCombTok tokens x kCombCols columns.
+// ---------------------------------------------------------------------------
+constexpr int kCombTok = 16;
+constexpr int kCombCols = 256;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+constexpr int kHistEntries = 16384;   // n_route * E must fit (int32, in LDS)
+
+enum : int { EV_ROUTE = 0, EV_SCAN = 1, EV_GROUP = 2, EV_G1ALL = 3, EV_DOWN = 4, EV_FIXED = 8 };
+
+// per-call metadata words (HDR_META + i), written by the scan task
+enum : int { MD_NB = 0, MD_TOTAL1 = 1, MD_TOTAL2 = 2, MD_NCOMB = 3 };
+
+struct MoePlan {
+  int t_max, hidden, inter, n_experts, top_k, n_route;
+  ET_HD int nb_max() const { return cdiv(t_max * top_k, kMinRows) + n_experts; }
+  ET_HD int ev_exp() const { return EV_FIXED; }
+  ET_HD int ev_h() const { return EV_FIXED + n_experts; }
+  ET_HD int ev_c() const { return ev_h() + nb_max(); }
+  ET_HD int n_events_max() const { return ev_c() + t_max * (hidden / kMinCols); }
+  ET_HD int extent(int T, const Tiling& t) const { return ev_c() + T * (hidden / t.bn2); }
+  ET_HD int n_comb(int T) const { return cdiv(T, kCombTok) * cdiv(hidden, kCombCols); }
+  ET_HD int max_tasks() const {
+    return 2 * n_route + 1 + nb_max() * (inter / kMinCols + hidden / kMinCols) + n_comb(t_max);
+  }
+  ET_HD int tpr(int T) const { return cdiv(T, n_route); }
+};
+
+ET_HD int moe_n_route(int n_experts) {
+  int r = kHistEntries / n_experts;
+  return r > 128 ? 128 : (r < 1 ? 1 : r);
+}
+
+// Byte offsets of the MoE intermediates inside the aux region.
+struct MoeAux {
+  size_t topk_ids, topk_w, hist, counts, tok_indptr, blk_indptr, task_indptr, blk_expert,
+      perm, inv, h, y, bytes;
+};
+
+inline MoeAux moe_aux_layout(const MoePlan& p) {
+  MoeAux a;
+  size_t o = 0;
+  const size_t TK = (size_t)p.t_max * p.top_k;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes, 256); return r; };
+  a.topk_ids = take(TK * 4);
+  a.topk_w = take(TK * 4);
+  a.hist = take((size_t)p.n_route * p.n_experts * 4);
+  a.counts = take((size_t)p.n_experts * 4);
+  a.tok_indptr = take((size_t)(p.n_experts + 1) * 4);
+  a.blk_indptr = take((size_t)(p.n_experts + 1) * 4);
+  a.task_indptr = take((size_t)(p.n_experts + 1) * 4);
+  a.blk_expert = take((size_t)p.nb_max() * 4);
+  a.perm = take(TK * 4);
+  a.inv = take(TK * 4);
+  a.h = take(TK * p.inter * 2);
+  a.y = take(TK * p.hidden * 4);
+  a.bytes = o;
+  return a;
+}
+
+}  // namespace et

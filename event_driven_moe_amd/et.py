@@ -1,0 +1,253 @@
+"""Thin Python binding of the C ABI in include/et.h (argument marshalling only).
+
+Every function here checks dtypes, devices and shapes, then passes raw device
+pointers and the current HIP stream to libet.so.  All computation happens in
+the library's kernels; if libet.so is missing or cannot be loaded the calls
+raise, there is no fallback.
+"""
+
+import ctypes
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libet.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "et.h")
+
+SCHED_STATIC, SCHED_DYNAMIC, SCHED_BARRIER, SCHED_PER_OP = 0, 1, 2, 3
+SCHEDS = {"static": 0, "dynamic": 1, "barrier": 2, "per_op": 3}
+OK, EINVAL, EWORKSPACE, EHIP, ETIMEOUT, EUNSUPPORTED, ESTATE = range(7)
+WL_SPLITK, WL_MLP, WL_MOE = 1, 2, 3
+DEBUG_COUNTS = 1
+
+c_int, c_size_t, c_void_p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [("fetch_batch", c_int), ("debug_flags", c_int), ("timeout_ms", c_int),
+                ("tile", c_int)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("workload", c_int), ("max_tokens", c_int), ("hidden", c_int), ("inter", c_int),
+                ("n_experts", c_int), ("top_k", c_int), ("n_events", c_int),
+                ("max_tasks", c_int), ("bytes", c_size_t), ("off_counters", c_size_t),
+                ("off_slots", c_size_t), ("off_runs", c_size_t), ("off_aux", c_size_t),
+                ("aux_bytes", c_size_t)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("counters_bank", c_size_t * 2), ("n_events", c_int), ("runs", c_size_t),
+                ("topk_ids", c_size_t), ("topk_w", c_size_t), ("counts", c_size_t),
+                ("tok_indptr", c_size_t), ("perm", c_size_t), ("inv", c_size_t),
+                ("task_indptr", c_size_t), ("h", c_size_t)]
+
+
+class Report(ctypes.Structure):
+    _fields_ = [("status", c_int), ("err_info", c_int * 3), ("bank", c_int), ("calls", c_int),
+                ("last_tasks", c_int), ("q_head", c_int), ("q_push", c_int),
+                ("last_extent", c_int)]
+
+
+class EtError(RuntimeError):
+    def __init__(self, code, what):
+        super().__init__("%s: %s (status %d)" % (what, status_str(code), code))
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Loads libet.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libet.so is not built; run __graft_entry__.build() or "
+                               "python -m event_driven_moe_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        L.et_plan_workspace.argtypes = [c_int] * 6 + [P(Plan)]
+        L.et_workspace_init.argtypes = [c_void_p, P(Plan), c_void_p]
+        L.et_workspace_layout.argtypes = [P(Plan), c_int, P(Layout)]
+        L.et_splitk_reduce.argtypes = [c_void_p, c_int, c_void_p, c_void_p, c_void_p, P(Plan),
+                                       c_int, P(Opts), c_void_p]
+        L.et_mlp.argtypes = [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                             P(Plan), c_int, P(Opts), c_void_p]
+        L.et_moe_layer.argtypes = [c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p,
+                                   c_void_p, c_void_p, P(Plan), c_int, P(Opts), c_void_p]
+        L.et_read_status.argtypes = [c_void_p, P(Plan), c_void_p, P(Report)]
+        L.et_status_str.argtypes = [c_int]
+        L.et_status_str.restype = ctypes.c_char_p
+        L.et_num_workers.argtypes = []
+        for f in ("et_plan_workspace", "et_workspace_init", "et_workspace_layout",
+                  "et_splitk_reduce", "et_mlp", "et_moe_layer", "et_read_status",
+                  "et_num_workers"):
+            getattr(L, f).restype = c_int
+        _lib = L
+    return _lib
+
+
+def header_functions():
+    """Names of the functions include/et.h declares."""
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(et_[a-z_0-9]+)\s*\(", src)))
+
+
+def status_str(code):
+    try:
+        return lib().et_status_str(int(code)).decode()
+    except RuntimeError:
+        return "status %d" % code
+
+
+def _check(code, what):
+    if code != OK:
+        raise EtError(code, what)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return c_void_p(stream.cuda_stream)
+
+
+def _ptr(t, dtype, name, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return c_void_p(t.data_ptr())
+
+
+def _opts(fetch_batch=4, debug=0, timeout_ms=2000, tile=-1):
+    return Opts(fetch_batch, debug, timeout_ms, tile)
+
+
+def plan_workspace(workload, max_tokens, hidden=0, inter=0, n_experts=0, top_k=0):
+    p = Plan()
+    _check(lib().et_plan_workspace(workload, max_tokens, hidden, inter, n_experts, top_k,
+                                   ctypes.byref(p)), "et_plan_workspace")
+    return p
+
+
+class Workspace:
+    """Device memory for one workload's event counters, ready queue and
+    intermediates, sized by et_plan_workspace and cleared by et_workspace_init."""
+
+    def __init__(self, workload, max_tokens, hidden=0, inter=0, n_experts=0, top_k=0,
+                 device="cuda", stream=None):
+        self.plan = plan_workspace(workload, max_tokens, hidden, inter, n_experts, top_k)
+        self.buf = torch.empty(self.plan.bytes, dtype=torch.uint8, device=device)
+        self.init(stream)
+
+    def init(self, stream=None):
+        _check(lib().et_workspace_init(c_void_p(self.buf.data_ptr()), ctypes.byref(self.plan),
+                                       _stream(stream)), "et_workspace_init")
+
+    @property
+    def ptr(self):
+        return c_void_p(self.buf.data_ptr())
+
+    def layout(self, n_tokens=0):
+        lay = Layout()
+        _check(lib().et_workspace_layout(ctypes.byref(self.plan), n_tokens, ctypes.byref(lay)),
+               "et_workspace_layout")
+        return lay
+
+    def view(self, offset, dtype, count):
+        """A typed view of `count` elements at byte `offset` of the workspace."""
+        nbytes = torch.empty((), dtype=dtype).element_size() * count
+        return self.buf[offset:offset + nbytes].view(dtype)
+
+    def status(self, stream=None):
+        r = Report()
+        _check(lib().et_read_status(self.ptr, ctypes.byref(self.plan), _stream(stream),
+                                    ctypes.byref(r)), "et_read_status")
+        return {"status": r.status, "err_info": list(r.err_info), "bank": r.bank,
+                "calls": r.calls, "last_tasks": r.last_tasks, "q_head": r.q_head,
+                "q_push": r.q_push, "last_extent": r.last_extent}
+
+    def counters(self, bank):
+        lay = self.layout()
+        return self.view(lay.counters_bank[bank], torch.int32, lay.n_events)
+
+    def runs(self):
+        lay = self.layout()
+        return self.view(lay.runs, torch.int32, self.plan.max_tasks)
+
+
+def splitk_reduce(A, Bpart, C, ws, sched="static", stream=None, **opts):
+    rows = A.shape[0]
+    a = _ptr(A, torch.float32, "A", (rows, 128))
+    b = _ptr(Bpart, torch.float32, "Bpart", (rows, 4))
+    c = _ptr(C, torch.float32, "C", (rows,))
+    o = _opts(**opts)
+    _check(lib().et_splitk_reduce(a, rows, b, c, ws.ptr, ctypes.byref(ws.plan),
+                                  SCHEDS.get(sched, sched), ctypes.byref(o), _stream(stream)),
+           "et_splitk_reduce")
+
+
+def mlp(x, w_gate, w_up, w_down, y, ws, sched="static", stream=None, **opts):
+    """x bf16 [B,H]; w_gate/w_up bf16 [I,H] (K-contiguous); w_down bf16 [H,I]; y f32 [B,H]."""
+    B, H = x.shape
+    I = w_gate.shape[0]
+    args = (_ptr(x, torch.bfloat16, "x", (B, H)), B,
+            _ptr(w_gate, torch.bfloat16, "w_gate", (I, H)),
+            _ptr(w_up, torch.bfloat16, "w_up", (I, H)),
+            _ptr(w_down, torch.bfloat16, "w_down", (H, I)),
+            _ptr(y, torch.float32, "y", (B, H)))
+    if (H, I) != (ws.plan.hidden, ws.plan.inter):
+        raise ValueError("weights do not match the workspace plan")
+    o = _opts(**opts)
+    _check(lib().et_mlp(*args, ws.ptr, ctypes.byref(ws.plan), SCHEDS.get(sched, sched),
+                        ctypes.byref(o), _stream(stream)), "et_mlp")
+
+
+def moe_layer(logits, x, w_gate, w_up, w_down, out, ws, sched="dynamic", stream=None, **opts):
+    """logits f32 [T,E]; x bf16 [T,H]; w_gate/w_up bf16 [E,I,H]; w_down bf16 [E,H,I];
+    out f32 [T,H]."""
+    T, E = logits.shape
+    H = x.shape[1]
+    I = w_gate.shape[1]
+    args = (_ptr(logits, torch.float32, "logits", (T, E)), _ptr(x, torch.bfloat16, "x", (T, H)),
+            T, _ptr(w_gate, torch.bfloat16, "w_gate", (E, I, H)),
+            _ptr(w_up, torch.bfloat16, "w_up", (E, I, H)),
+            _ptr(w_down, torch.bfloat16, "w_down", (E, H, I)),
+            _ptr(out, torch.float32, "out", (T, H)))
+    if (H, I, E) != (ws.plan.hidden, ws.plan.inter, ws.plan.n_experts):
+        raise ValueError("weights do not match the workspace plan")
+    o = _opts(**opts)
+    _check(lib().et_moe_layer(*args, ws.ptr, ctypes.byref(ws.plan), SCHEDS.get(sched, sched),
+                              ctypes.byref(o), _stream(stream)), "et_moe_layer")
+
+
+def moe_aux(ws, T):
+    """Routing results and grouping of the last call (views into the workspace)."""
+    lay = ws.layout(T)
+    k, E = ws.plan.top_k, ws.plan.n_experts
+    return {
+        "ids": ws.view(lay.topk_ids, torch.int32, T * k).view(T, k),
+        "w": ws.view(lay.topk_w, torch.float32, T * k).view(T, k),
+        "counts": ws.view(lay.counts, torch.int32, E),
+        "tok_indptr": ws.view(lay.tok_indptr, torch.int32, E + 1),
+        "perm": ws.view(lay.perm, torch.int32, T * k),
+        "inv": ws.view(lay.inv, torch.int32, T * k).view(T, k),
+        "task_indptr": ws.view(lay.task_indptr, torch.int32, E + 1),
+    }
+
+
+def num_workers():
+    n = lib().et_num_workers()
+    if n < 0:
+        raise EtError(-n, "et_num_workers")
+    return n

@@ -50,7 +50,7 @@ def _gen(seed, device):
     return g
 
 
-def _normal_bf16(shape, std, seed, device):
+def normal_bf16(shape, std, seed, device):
     g = _gen(seed, device)
     v = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
     if std != 1.0:
@@ -69,10 +69,10 @@ def splitk_inputs(rows=2048, seed=101, device="cpu", integer=False):
 def mlp_inputs(batch, hidden=2048, inter=5632, device="cpu", seeds=(201, 202, 203, 204)):
     """x [B,H], wg [H,I], wu [H,I], wd [I,H] (bf16, logical layout)."""
     sx, sg, su, sd = seeds
-    x = _normal_bf16((batch, hidden), 1.0, sx + batch, device)
-    wg = _normal_bf16((hidden, inter), WEIGHT_STD, sg, device)
-    wu = _normal_bf16((hidden, inter), WEIGHT_STD, su, device)
-    wd = _normal_bf16((inter, hidden), WEIGHT_STD, sd, device)
+    x = normal_bf16((batch, hidden), 1.0, sx + batch, device)
+    wg = normal_bf16((hidden, inter), WEIGHT_STD, sg, device)
+    wu = normal_bf16((hidden, inter), WEIGHT_STD, su, device)
+    wd = normal_bf16((inter, hidden), WEIGHT_STD, sd, device)
     return x, wg, wu, wd
 
 
@@ -100,7 +100,7 @@ def moe_activations(cfg, tokens, device="cpu"):
     g = _gen(cfg["seed_logits"] + tokens, device)
     logits = torch.randn((tokens, E), generator=g, device=device, dtype=torch.float32)
     logits += expert_bias(cfg, tokens, device)[None, :]
-    x = _normal_bf16((tokens, H), 1.0, cfg["seed_x"] + tokens, device)
+    x = normal_bf16((tokens, H), 1.0, cfg["seed_x"] + tokens, device)
     return logits, x
 
 
@@ -112,9 +112,9 @@ def expert_seed(cfg, e, which):
 def moe_expert_weights(cfg, e, device="cpu"):
     """Expert e's logical weights: wg [H,I], wu [H,I], wd [I,H] (bf16)."""
     H, I = cfg["hidden"], cfg["inter"]
-    return (_normal_bf16((H, I), WEIGHT_STD, expert_seed(cfg, e, 0), device),
-            _normal_bf16((H, I), WEIGHT_STD, expert_seed(cfg, e, 1), device),
-            _normal_bf16((I, H), WEIGHT_STD, expert_seed(cfg, e, 2), device))
+    return (normal_bf16((H, I), WEIGHT_STD, expert_seed(cfg, e, 0), device),
+            normal_bf16((H, I), WEIGHT_STD, expert_seed(cfg, e, 1), device),
+            normal_bf16((I, H), WEIGHT_STD, expert_seed(cfg, e, 2), device))
 
 
 def moe_weights_k_major(cfg, device="cpu", experts=None):

@@ -1,0 +1,179 @@
+"""GPU parity: the MoE layer vs the oracle (small and skewed layers)."""
+
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+from event_driven_moe_amd import et, synth
+from oracle import moe as omoe, events as oev
+from gpu_helpers import DEV, SCHEDS, say, assert_rel, to_np, moe_weights, moe_oracle_weights
+
+pytestmark = pytest.mark.gpu
+
+
+@functools.lru_cache(maxsize=4)
+def _ws(name, max_tokens):
+    cfg = synth.MOE_PRESETS[name]
+    return et.Workspace(et.WL_MOE, max_tokens, cfg["hidden"], cfg["inter"], cfg["n_experts"],
+                        cfg["top_k"], device=DEV)
+
+
+def run_moe(name, T, sched, ws=None, **opts):
+    cfg = synth.MOE_PRESETS[name]
+    wg, wu, wd = moe_weights(name)
+    logits, x = synth.moe_activations(cfg, T, device=DEV)
+    ws = ws or _ws(name, max(cfg["tokens"]))
+    out = torch.full((T, cfg["hidden"]), float("nan"), device=DEV)
+    say("moe", name, T, sched, opts)
+    et.moe_layer(logits, x, wg, wu, wd, out, ws, sched, **opts)
+    torch.cuda.synchronize()
+    st = ws.status()
+    assert st["status"] == 0, st
+    aux = {k: v.cpu().numpy() for k, v in et.moe_aux(ws, T).items()}
+    return cfg, logits, x, (wg, wu, wd), out.cpu().numpy(), aux, ws
+
+
+@functools.lru_cache(maxsize=8)
+def _oracle(name, T):
+    cfg = synth.MOE_PRESETS[name]
+    wg, wu, wd = moe_weights(name)
+    logits, x = synth.moe_activations(cfg, T, device=DEV)
+    return omoe.moe_layer(to_np(logits), to_np(x), cfg["top_k"], moe_oracle_weights(wg, wu, wd))
+
+
+def check_against_oracle(name, T, out, aux):
+    ref = _oracle(name, T)
+    assert np.array_equal(aux["ids"], ref["ids"]), "topk ids"
+    assert np.array_equal(aux["counts"], ref["counts"]), "counts"
+    assert np.array_equal(aux["tok_indptr"], ref["tok_indptr"]), "tok_indptr"
+    assert np.array_equal(aux["perm"], ref["perm"]), "perm"
+    assert np.array_equal(aux["inv"], ref["inv"]), "inv"
+    assert np.abs(aux["w"] - ref["w"]).max() <= 1e-5 * np.abs(ref["w"]).max(), "topk_w"
+    assert_rel(out, ref["out"], 1e-2, "out")
+    return ref
+
+
+CASES = [("moe_small", 1), ("moe_small", 8), ("moe_small", 32),
+         ("moe_skewed", 64), ("moe_skewed", 256), ("moe_skewed", 1024)]
+
+
+@pytest.mark.parametrize("sched", SCHEDS)
+@pytest.mark.parametrize("name,T", CASES)
+def test_parity(name, T, sched):
+    _, _, _, _, out, aux, _ = run_moe(name, T, sched)
+    check_against_oracle(name, T, out, aux)
+
+
+@pytest.mark.parametrize("name,T", [("moe_small", 32), ("moe_skewed", 256)])
+def test_modes_bit_identical(name, T):
+    outs = [run_moe(name, T, s)[4] for s in SCHEDS]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2])
+def test_tile_variants(tile):
+    _, _, _, _, out, aux, _ = run_moe("moe_skewed", 64, "dynamic", tile=tile)
+    check_against_oracle("moe_skewed", 64, out, aux)
+
+
+@pytest.mark.parametrize("fetch", [1, 8])
+def test_fetch_batches(fetch):
+    _, _, _, _, out, aux, _ = run_moe("moe_skewed", 256, "dynamic", fetch_batch=fetch)
+    check_against_oracle("moe_skewed", 256, out, aux)
+
+
+@pytest.mark.parametrize("sched", ["static", "dynamic"])
+def test_event_invariants(sched):
+    """Each task ran once; the data-dependent expert events ended at their
+    run-time wait counts (rows routed to each expert), block events at the
+    number of gate/up tiles of a block."""
+    name, T = "moe_skewed", 256
+    ws = _ws(name, 1024)
+    ws.runs().zero_()
+    cfg, _, _, _, out, aux, _ = run_moe(name, T, sched, ws=ws, debug=et.DEBUG_COUNTS)
+    st = ws.status()
+    E, k, H, I = cfg["n_experts"], cfg["top_k"], cfg["hidden"], cfg["inter"]
+    nr = min(128, 16384 // E)
+    rows = 64          # T = 256 -> 64-row tiles
+    tab = oev.moe_table(aux["counts"], rows, I, 16, H, 16, nr)
+    ncomb = -(-T // 16) * -(-H // 256) if sched == "static" else 0
+    total = sum(tab["tasks"].values()) + ncomb
+    runs = ws.runs().cpu().numpy()
+    assert (runs[:total] == 1).all() and (runs[total:] == 0).all()
+    cnt = ws.counters(1 - st["bank"]).cpu().numpy()
+    assert cnt[0] == -nr                                   # all routing tasks notified
+    ev_exp, ev_h = 8, 8 + E
+    nb = tab["blocks"]
+    assert (cnt[ev_h:ev_h + nb] == -tab["events"]["E_h"]["wait_count"]).all()
+    if sched == "dynamic":
+        assert (cnt[ev_exp:ev_exp + E] == -tab["events"]["E_exp"]["wait_count"]).all()
+        nb_max = -(-1024 * k // 16) + E
+        ev_c = ev_h + nb_max
+        assert (cnt[ev_c:ev_c + T * (H // 16)] == -k).all()
+    else:
+        assert cnt[1] == -1 and cnt[2] == -nr and cnt[4] == -(nb * (H // 16))
+    check_against_oracle(name, T, out, aux)
+
+
+def _exact_case(k, E=4, H=256, I=256, T=50, seed=0):
+    """Integer experts: x in {0,1} with x[:,0]=1; gate row 0 in [16,40) so
+    SiLU(g) == g below bf16 precision; |u| <= 6, so h = g*u exactly; down in
+    {-2..2}: every y is an exact fp32 integer.  Logits make the kept weights
+    exactly 1 (k = 1) or 1/2 (two tied maxima, k = 2)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    x = torch.randint(0, 2, (T, H), generator=g).float()
+    x[:, 0] = 1
+    wg = torch.zeros(E, H, I)
+    wg[:, 0, :] = torch.randint(16, 40, (E, I), generator=g).float()
+    wu = torch.zeros(E, H, I)
+    for e in range(E):
+        for i in range(I):
+            r = torch.randperm(H - 1, generator=g)[:6] + 1
+            wu[e, r, i] = torch.randint(0, 2, (6,), generator=g).float() * 2 - 1
+    wd = torch.randint(-2, 3, (E, I, H), generator=g).float()
+    logits = torch.randn(T, E, generator=g) - 4.0
+    for t in range(T):
+        logits[t, torch.randperm(E, generator=g)[:k]] = 1.0   # ties between k distinct experts
+    return x, wg, wu, wd, logits
+
+
+@pytest.mark.parametrize("k", [1, 2])
+@pytest.mark.parametrize("sched", ["static", "dynamic"])
+def test_integer_exact(k, sched):
+    x, wg, wu, wd, logits = _exact_case(k)
+    E, H, I = wg.shape[0], wg.shape[1], wg.shape[2]
+    T = x.shape[0]
+    ws = et.Workspace(et.WL_MOE, 64, H, I, E, k, device=DEV)
+    out = torch.full((T, H), float("nan"), device=DEV)
+    dev = lambda t: t.to(torch.bfloat16).to(DEV)
+    say("moe integer", k, sched)
+    et.moe_layer(logits.to(DEV), dev(x), synth.k_major(dev(wg)), synth.k_major(dev(wu)),
+                 synth.k_major(dev(wd)), out, ws, sched)
+    torch.cuda.synchronize()
+    assert ws.status()["status"] == 0
+    ref = omoe.moe_layer(logits.numpy(), x.numpy(), k, (wg.numpy(), wu.numpy(), wd.numpy()))
+    ids, w = ref["ids"], ref["w"]
+    assert set(np.unique(w).tolist()) <= {1.0, 0.5}
+    exact = np.zeros((T, H))
+    for t in range(T):
+        for s in range(k):
+            e = ids[t, s]
+            gg = x[t].numpy().astype(np.float64) @ wg[e].numpy()
+            uu = x[t].numpy().astype(np.float64) @ wu[e].numpy()
+            exact[t] += w[t, s] * ((gg * uu) @ wd[e].numpy())
+    assert np.array_equal(out.cpu().numpy(), exact.astype(np.float32))
+    aux = {kk: v.cpu().numpy() for kk, v in et.moe_aux(ws, T).items()}
+    assert np.array_equal(aux["ids"], ids) and np.array_equal(aux["perm"], ref["perm"])
+
+
+def test_symbolic_token_counts_one_workspace():
+    """One workspace, token counts changing call to call (and the tile variant
+    with them): every call still matches the oracle."""
+    ws = _ws("moe_skewed", 1024)
+    for T in (64, 1, 1024, 17, 33):
+        for sched in ("dynamic", "static"):
+            _, _, _, _, out, aux, _ = run_moe("moe_skewed", T, sched, ws=ws)
+            check_against_oracle("moe_skewed", T, out, aux)
