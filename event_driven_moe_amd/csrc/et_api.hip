@@ -20,6 +20,7 @@ RunArgs LaunchCommon::run_args() const {
   a.slots = reinterpret_cast<int*>(ws + plan->off_slots);
   a.q_cap = plan->max_tasks;
   a.runs = (debug & ET_DEBUG_COUNTS) ? reinterpret_cast<int*>(ws + plan->off_runs) : nullptr;
+  a.trace = (debug & ET_DEBUG_TRACE) ? reinterpret_cast<int*>(ws + plan->off_trace) : nullptr;
   a.sched = sched;
   a.fetch = fetch;
   a.phase = -1;
@@ -127,7 +128,7 @@ int et_plan_workspace(int workload, int max_tokens, int hidden, int inter, int n
     if (n_experts > kMaxExperts || top_k > kMaxTopK) return ET_EUNSUPPORTED;
     const size_t tk = (size_t)max_tokens * top_k;
     if (tk * inter * 2 >= (1ull << 31) || (size_t)max_tokens * hidden * 2 >= (1ull << 31) ||
-        (size_t)inter * hidden * 2 >= (1ull << 31) || tk * hidden * 4 >= (1ull << 34))
+        (size_t)inter * hidden * 2 >= (1ull << 31) || tk * hidden * 4 >= (1ull << 31))
       return ET_EUNSUPPORTED;
     MoePlan p{max_tokens, hidden, inter, n_experts, top_k, moe_n_route(n_experts)};
     if ((size_t)p.n_events_max() >= (1ull << 30) || (size_t)p.max_tasks() >= (1ull << 30))
@@ -149,6 +150,8 @@ int et_plan_workspace(int workload, int max_tokens, int hidden, int inter, int n
   o = align_up(o + (size_t)plan->max_tasks * 4, 256);
   plan->off_runs = o;
   o = align_up(o + (size_t)plan->max_tasks * 4, 256);
+  plan->off_trace = o;
+  o = align_up(o + (size_t)plan->max_tasks * 16 + 1024 * 8, 256);
   plan->off_aux = o;
   plan->aux_bytes = aux;
   plan->bytes = align_up(o + aux, 256);
@@ -171,6 +174,7 @@ int et_workspace_layout(const et_plan* plan, int n_tokens, et_layout* out) {
   out->counters_bank[1] = plan->off_counters + (size_t)plan->n_events * 4;
   out->n_events = plan->n_events;
   out->runs = plan->off_runs;
+  out->trace = plan->off_trace;
   if (plan->workload == ET_WL_MLP) {
     out->h = plan->off_aux;
   } else if (plan->workload == ET_WL_MOE) {

@@ -19,9 +19,17 @@
 // leave flips the bank.  No host memset and no grid barrier are needed.
 //
 // Memory ordering: producers and consumers run on different compute units,
-// often on different XCDs with separate L2 caches.  notify() makes every wave
-// of the producer perform an agent-scope release before the workgroup barrier
-// and the decrement; wait() and queue pops end with an agent-scope acquire.
+// often on different XCDs with separate L2 caches.  Agent-scope fences would
+// write back and invalidate a whole XCD's L2 at every notify and wait, which
+// destroys the L2 reuse the GEMM tasks depend on.  Instead, every access to
+// data that another workgroup of the same launch produced or will consume
+// (intermediates, routing results, counters, queue slots) is itself
+// agent-coherent -- the sc1 loads and stores that agent-scope monotonic
+// atomics lower to -- and notify() first waits until all of the workgroup's
+// stores have completed (s_waitcnt vmcnt(0) in every wave, then the workgroup
+// barrier) before the decrement.  A consumer that observes the fired counter
+// then reads the producers' data with coherent loads.  Inputs that no task
+// writes (x, weights, logits) use ordinary cached loads.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,31 +41,26 @@
 namespace et {
 
 // ---------------------------------------------------------------------------
-// atomics and fences (agent scope = the whole GPU)
+// agent-coherent accesses (agent scope = the whole GPU)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ long long now_ticks() {
   return (long long)__builtin_amdgcn_s_memrealtime();   // constant 100 MHz clock
 }
-__device__ __forceinline__ int ld_rlx(const int* p) {
+template <class T>
+__device__ __forceinline__ T ld_coh(const T* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_rlx(int* p, int v) {
+template <class T>
+__device__ __forceinline__ void st_coh(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void st_rel(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
+__device__ __forceinline__ int ld_rlx(const int* p) { return ld_coh(p); }
+__device__ __forceinline__ void st_rlx(int* p, int v) { st_coh(p, v); }
 __device__ __forceinline__ int add_rlx(int* p, int v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ int add_rel(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int add_acqrel(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_mem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
 // per-call arguments and context
@@ -69,11 +72,13 @@ struct RunArgs {
   int* slots;          // ready-queue slots (pushed tasks; implicit initial tasks need none)
   int q_cap;
   int* runs;           // per-task run counts, or nullptr
+  int* trace;          // per-task trace records, or nullptr
   int sched;           // ET_SCHED_*
   int fetch;           // dynamic: slots claimed per atomic
   int phase;           // per-op mode: operator this launch runs
   long long timeout;   // watchdog, 100 MHz ticks
   int n_init;          // dynamic: tasks [0, n_init) are in the queue from the start
+  int n_single;        // dynamic: slots below this index are claimed one at a time
   int total_hint;      // dynamic: total tasks when known at launch, else kUnknownTotal
   int extent;          // counters this call uses (a prefix of its bank)
 };
@@ -141,41 +146,78 @@ __device__ __noinline__ int spin_until(const Ctx& c, int idx, int wait_count, in
 // `wait_count` notifies.  Returns false when the call is being abandoned.
 __device__ __forceinline__ bool wg_wait(const Ctx& c, int idx, int wait_count, int task) {
   int ok = 1;
-  if (threadIdx.x == 0) {
-    ok = spin_until(c, idx, wait_count, task);
-    fence_acquire();
-  }
+  if (threadIdx.x == 0) ok = spin_until(c, idx, wait_count, task);
   return wg_bcast(c, ok, 1) != 0;
 }
 
-// Several events at once (all must fire).
+// Several consecutive events at once (all must fire): the lanes of wave 0
+// check up to 64 counters per memory round trip.
+__device__ __noinline__ int spin_until_all(const Ctx& c, int first, int n, int wait_count,
+                                           int task) {
+  const int lane = threadIdx.x & 63;
+  const int target = -wait_count;
+  long long t0 = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int idx = first + base + lane;
+    const bool mine = base + lane < n;
+    for (int it = 0;; ++it) {
+      const int v = mine ? ld_rlx(c.ev + idx) : target;
+      if (v < target) raise_fault(c.a, ET_ESTATE, task, idx, v);
+      const unsigned long long pending = __ballot(v != target);
+      if (pending == 0) break;
+      if (__ballot(v < target) != 0) return 0;
+      if (it == 0) t0 = now_ticks();
+      __builtin_amdgcn_s_sleep(1);
+      if ((it & 63) == 63) {
+        if (faulted(c.a)) return 0;
+        if (now_ticks() - t0 > c.a.timeout) {
+          if (lane == 0) raise_fault(c.a, ET_ETIMEOUT, task, first + base, n);
+          return 0;
+        }
+      }
+    }
+  }
+  return 1;
+}
+
 __device__ __forceinline__ bool wg_wait_range(const Ctx& c, int first, int n, int wait_count,
                                               int task) {
   int ok = 1;
-  if (threadIdx.x == 0) {
-    for (int i = 0; i < n && ok; ++i) ok = spin_until(c, first + i, wait_count, task);
-    fence_acquire();
-  }
+  if (threadIdx.x < 64) ok = spin_until_all(c, first, n, wait_count, task);
   return wg_bcast(c, ok, 1) != 0;
 }
 
-// Publish this workgroup's global stores at agent scope (every wave), then
-// synchronise the workgroup.  Precedes every notify.
+// Non-blocking: have all of events [first, first + n) fired?  One memory
+// round trip per 64 events (wave 0's lanes), result broadcast.
+__device__ __forceinline__ bool wg_probe_range(const Ctx& c, int first, int n, int wait_count) {
+  int all = 1;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    for (int base = 0; base < n && all; base += 64) {
+      const bool mine = base + lane < n;
+      const int v = mine ? ld_rlx(c.ev + first + base + lane) : -wait_count;
+      all = __ballot(v != -wait_count) == 0;
+    }
+  }
+  return wg_bcast(c, all, 1) != 0;
+}
+
+// Complete this workgroup's stores (every wave), then synchronise the
+// workgroup.  Precedes every notify and push.
 __device__ __forceinline__ void wg_release() {
-  fence_release();
+  wait_mem();
   __syncthreads();
 }
 
 // notify(): decrement event `idx` by n.  Must follow wg_release().  Returns
-// (to every thread) whether this notify fired the event.  With `acquire`, the
-// firing workgroup also acquires what the other notifiers published (needed
-// when it goes on to push or run the consumers).
-__device__ __forceinline__ bool wg_notify(const Ctx& c, int idx, int n, int wait_count, int task,
-                                          bool acquire) {
+// (to every thread) whether this notify fired the event, i.e. brought it to
+// its wait count; every other notifier had completed its stores before its
+// own decrement, so the firing workgroup may push or run the consumers.
+__device__ __forceinline__ bool wg_notify(const Ctx& c, int idx, int n, int wait_count, int task) {
   int fired = 0;
   if (threadIdx.x == 0) {
     int* p = c.ev + idx;
-    int old = acquire ? add_acqrel(p, -n) : add_rel(p, -n);
+    int old = add_rlx(p, -n);
     int now = old - n;
     if (now < -wait_count) raise_fault(c.a, ET_ESTATE, task, idx, now);
     fired = now == -wait_count;
@@ -183,15 +225,18 @@ __device__ __forceinline__ bool wg_notify(const Ctx& c, int idx, int n, int wait
   return wg_bcast(c, fired, 2) != 0;
 }
 
-// Thread-0-only notify (no broadcast), for fire-and-forget notifies after wg_release().
+// Thread-0-only notify (no broadcast, no returned value): fire-and-forget
+// after wg_release().  Over-notification is still caught by the waiter.
 __device__ __forceinline__ void t0_notify(const Ctx& c, int idx, int n, int wait_count, int task) {
-  if (threadIdx.x == 0) {
-    int old = add_rel(c.ev + idx, -n);
-    if (old - n < -wait_count) raise_fault(c.a, ET_ESTATE, task, idx, old - n);
-  }
+  (void)wait_count;
+  (void)task;
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(c.ev + idx, -n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// push(): append tasks id_of(0..n-1) to the ready queue.  Whole workgroup.
+// push(): append tasks id_of(0..n-1) to the ready queue.  Whole workgroup;
+// must follow wg_release() (or a fired wg_notify) so the pushed tasks' inputs
+// are complete before their slots are published.
 template <class F>
 __device__ __forceinline__ void wg_push(const Ctx& c, int n, F id_of) {
   if (n <= 0) return;
@@ -201,7 +246,7 @@ __device__ __forceinline__ void wg_push(const Ctx& c, int n, F id_of) {
   for (int i = threadIdx.x; i < n; i += kThreads) {
     int s = base + i;
     if (s < c.a.q_cap)
-      st_rel(&c.a.slots[s], id_of(i) + 1);
+      st_rlx(&c.a.slots[s], id_of(i) + 1);
     else
       raise_fault(c.a, ET_ESTATE, -1, s, c.a.q_cap);
   }
@@ -215,6 +260,7 @@ __device__ __forceinline__ void set_total(const Ctx& c, int total) {
 // Worker-side claim state (meaningful in thread 0 only).
 struct PopState {
   int base = 0;
+  int size = 0;
   int left = 0;
 };
 
@@ -232,7 +278,6 @@ __device__ __noinline__ int resolve_slot(const Ctx& c, int idx) {
       int v = ld_rlx(&c.a.slots[s]);
       if (v != 0) {
         st_rlx(&c.a.slots[s], 0);   // leave the slot empty for the next call
-        fence_acquire();
         return v - 1;
       }
     }
@@ -255,10 +300,15 @@ __device__ __forceinline__ int wg_pop(const Ctx& c, PopState& ps) {
   int t = -1;
   if (threadIdx.x == 0) {
     if (ps.left == 0) {
-      ps.base = add_rlx(&c.a.hdr[HDR_QHEAD], c.a.fetch);
-      ps.left = c.a.fetch;
+      // short leading phases (few, latency-critical tasks) are claimed one
+      // slot at a time so they spread over all workers; later, `fetch` slots
+      // per atomic (a racy peek is enough: any claim size is correct)
+      const int sz = ld_rlx(&c.a.hdr[HDR_QHEAD]) < c.a.n_single ? 1 : c.a.fetch;
+      ps.base = add_rlx(&c.a.hdr[HDR_QHEAD], sz);
+      ps.size = sz;
+      ps.left = sz;
     }
-    int idx = ps.base + (c.a.fetch - ps.left);
+    int idx = ps.base + (ps.size - ps.left);
     --ps.left;
     t = resolve_slot(c, idx);
   }
@@ -267,6 +317,24 @@ __device__ __forceinline__ int wg_pop(const Ctx& c, PopState& ps) {
 
 __device__ __forceinline__ void count_run(const Ctx& c, int task) {
   if (c.a.runs && threadIdx.x == 0) atomicAdd(&c.a.runs[task], 1);
+}
+
+// Debug trace: task -> (workgroup, start, end) in 100 MHz ticks.
+__device__ __forceinline__ long long trace_now(const Ctx& c) {
+  return c.a.trace ? now_ticks() : 0;
+}
+__device__ __forceinline__ void trace_task(const Ctx& c, int task, long long t0) {
+  if (c.a.trace && threadIdx.x == 0 && task >= 0 && task < c.a.q_cap) {
+    int* p = c.a.trace + 4 * (size_t)task;
+    p[0] = c.wg;
+    p[1] = (int)t0;
+    p[2] = (int)now_ticks();
+    p[3] = 1;
+  }
+}
+__device__ __forceinline__ void trace_wg(const Ctx& c, int which) {
+  if (c.a.trace && threadIdx.x == 0 && c.wg < 1024)
+    c.a.trace[4 * (size_t)c.a.q_cap + 2 * c.wg + which] = (int)now_ticks();
 }
 
 // Prologue: pick this call's bank and re-arm the part of the other bank the
@@ -279,6 +347,7 @@ __device__ __forceinline__ bool prologue(Ctx& c, const RunArgs& a, Shared* sh) {
   if (ld_rlx(&a.hdr[HDR_ERR]) != 0) return false;
   int bank = ld_rlx(&a.hdr[HDR_BANK]) & 1;
   c.ev = a.counters + (size_t)bank * a.n_events;
+  trace_wg(c, 0);
   if (a.sched != ET_SCHED_PER_OP) {
     int* other = a.counters + (size_t)(1 - bank) * a.n_events;
     int ext = ld_rlx(&a.hdr[HDR_EXT0 + (1 - bank)]);
@@ -291,11 +360,11 @@ __device__ __forceinline__ bool prologue(Ctx& c, const RunArgs& a, Shared* sh) {
 // Epilogue: the last workgroup out resets the queue, records the extent of
 // the bank it used and flips the bank for the next call.
 __device__ __forceinline__ void epilogue(const Ctx& c, int tasks_this_call) {
+  trace_wg(c, 1);
   if (c.a.sched == ET_SCHED_PER_OP) return;
   __syncthreads();
   if (threadIdx.x == 0) {
-    fence_release();
-    int old = add_acqrel(&c.a.hdr[HDR_EXIT], 1);
+    int old = add_rlx(&c.a.hdr[HDR_EXIT], 1);
     if (old == c.G - 1) {
       int* h = c.a.hdr;
       int bank = ld_rlx(&h[HDR_BANK]) & 1;
@@ -330,6 +399,17 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* p, uint32_t bytes) {
 __device__ __forceinline__ i32x4 ld16(Rsrc r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
+// agent-coherent 16-byte load (sc1): data written earlier in the same launch
+__device__ __forceinline__ i32x4 ld16c(Rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 16);
+}
+__device__ __forceinline__ void st16c(Rsrc r, uint32_t off, i32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 16);
+}
+template <bool COH>
+__device__ __forceinline__ i32x4 ld16x(Rsrc r, uint32_t off) {
+  return COH ? ld16c(r, off) : ld16(r, off);
+}
 
 __device__ __forceinline__ f32x4 mfma16(i32x4 a, i32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -344,5 +424,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// Wave-wide unsigned max / min through DPP lane moves (no LDS round trips):
+// quad permutes and row mirrors reduce each 16-lane row, two row broadcasts
+// fold the rows into lane 63, which is read back as a uniform value.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xf, 0xf, false));  // quad [1,0,3,2]
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xf, 0xf, false));  // quad [2,3,0,1]
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xf, 0xf, false)); // row half mirror
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x140, 0xf, 0xf, false)); // row mirror
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x142, 0xa, 0xf, false)); // row bcast 15
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x143, 0xc, 0xf, false)); // row bcast 31
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
 
 }  // namespace et

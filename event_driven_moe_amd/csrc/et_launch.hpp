@@ -43,12 +43,26 @@ int launch_mlp(const LaunchCommon& lc, const uint16_t* x, int B, const uint16_t*
 int launch_moe(const LaunchCommon& lc, const float* logits, const uint16_t* x, int T,
                const uint16_t* wg, const uint16_t* wu, const uint16_t* wd, float* out);
 
-// Tile variant for a call (rows per tile from the token count, unless forced).
-inline int pick_tile(int tokens_per_expert_bound, int forced) {
-  if (forced >= 0 && forced < TV_COUNT) return forced;
-  if (tokens_per_expert_bound <= 16) return TV_M16;
-  if (tokens_per_expert_bound <= 32) return TV_M32;
+// Dense MLP: rows per tile from the batch (stream variants only), unless forced.
+inline int pick_mlp_tile(int batch, int forced) {
+  if (forced >= 0 && forced <= TV_M64) return forced;
+  if (batch <= 16) return TV_M16;
+  if (batch <= 32) return TV_M32;
   return TV_M64;
+}
+
+// MoE: a token count bounds the rows any one expert receives (a token picks
+// an expert at most once); few rows -> narrow stream tiles, many rows -> wide
+// MFMA tiles.  `forced` (0 .. TV_COUNT-1) overrides.
+inline int pick_moe_tile(int tokens, int top_k, int n_experts, int forced) {
+  if (forced >= 0 && forced < TV_COUNT) return forced;
+  (void)top_k;
+  (void)n_experts;
+  if (tokens <= 16) return TV_M16;
+  if (tokens <= 32) return TV_M32;
+  if (tokens <= 128) return TV_M64;
+  if (tokens <= 512) return TV_W64;
+  return TV_W128;
 }
 
 }  // namespace et

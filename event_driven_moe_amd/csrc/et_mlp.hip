@@ -34,8 +34,8 @@ template <int MT>
 __global__ __launch_bounds__(kThreads, 1) void mlp_kernel(RunArgs ra, MlpArgs m) {
   __shared__ Shared sh;
   __shared__ uint32_t rows_off[16 * MT];
-  using Tile1 = StreamTile<MT, 2, 4, kMlpPD<MT>>;
-  using Tile2 = StreamTile<MT, 1, 4, kMlpPD<MT>>;
+  using Tile1 = StreamTile<MT, 2, 4, kMlpPD<MT>, false>;   // reads x
+  using Tile2 = StreamTile<MT, 1, 4, kMlpPD<MT>, true>;    // reads h (this launch)
   constexpr int kRed = Tile1::kRedFloats > Tile2::kRedFloats ? Tile1::kRedFloats : Tile2::kRedFloats;
   __shared__ float red[kRed];
 
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kThreads, 1) void mlp_kernel(RunArgs ra, MlpArgs m)
             const int row = b * rows + 16 * mt + 4 * (lane >> 4) + r;
             if (row < m.B) {
               const float g = tile.acc[mt][0][r], u = tile.acc[mt][1][r];
-              m.h[(size_t)row * m.I + 16 * n + (lane & 15)] = f32_to_bf16(silu(g) * u);
+              st_coh(&m.h[(size_t)row * m.I + 16 * n + (lane & 15)], f32_to_bf16(silu(g) * u));
             }
           }
       if (sched == ET_SCHED_PER_OP) return true;
@@ -98,9 +98,16 @@ __global__ __launch_bounds__(kThreads, 1) void mlp_kernel(RunArgs ra, MlpArgs m)
     const Rsrc rb[1] = {make_rsrc(m.wd, (uint32_t)m.H * m.I * 2)};
     const uint32_t bo[1] = {(uint32_t)(16 * n2 + (lane & 15)) * (uint32_t)(m.I * 2)};
     const int nkb = m.I / kKBlock;
+    bool ready = sched == ET_SCHED_PER_OP;
     auto gate = [&](int round) -> bool {
-      if (sched == ET_SCHED_PER_OP) return true;
+      if (ready) return true;
       if (sched == ET_SCHED_BARRIER) return round > 0 || wg_wait(c, m.ev_all, n_gate, task);
+      // one round trip checks every h tile of the row block; if some are not
+      // done yet, wait only for the K-blocks of the coming round
+      if (round == 0 && wg_probe_range(c, b * nht, nht, kHTile / 16)) {
+        ready = true;
+        return true;
+      }
       const int k0 = round * 4;
       const int nk = nkb - k0 < 4 ? nkb - k0 : 4;
       return wg_wait_range(c, b * nht + k0, nk, kHTile / 16, task);
@@ -127,24 +134,32 @@ __global__ __launch_bounds__(kThreads, 1) void mlp_kernel(RunArgs ra, MlpArgs m)
     PopState ps;
     for (;;) {
       const int t = wg_pop(c, ps);
+      const long long t0 = trace_now(c);
       if (t < 0 || !run(t)) break;
       count_run(c, t);
+      trace_task(c, t, t0);
     }
   } else if (sched == ET_SCHED_PER_OP) {
     const int lo = ra.phase == 0 ? 0 : n_gate, hi = ra.phase == 0 ? n_gate : total;
     for (int t = lo + c.wg; t < hi; t += c.G) {
+      const long long t0 = trace_now(c);
       run(t);
       count_run(c, t);
+      trace_task(c, t, t0);
     }
   } else {
     bool ok = true;
     for (int t = c.wg; ok && t < n_gate; t += c.G) {
+      const long long t0 = trace_now(c);
       ok = run(t);
       if (ok) count_run(c, t);
+      if (ok) trace_task(c, t, t0);
     }
     for (int t = n_gate + c.wg; ok && t < total; t += c.G) {
+      const long long t0 = trace_now(c);
       ok = run(t);
       if (ok) count_run(c, t);
+      if (ok) trace_task(c, t, t0);
     }
   }
   epilogue(c, total);
@@ -154,7 +169,7 @@ int launch_mlp(const LaunchCommon& lc, const uint16_t* x, int B, const uint16_t*
                const uint16_t* wu, const uint16_t* wd, float* y) {
   const et_plan* p = lc.plan;
   MlpPlan mp{p->max_tokens, p->hidden, p->inter};
-  const int tv = pick_tile(B, lc.tile);
+  const int tv = pick_mlp_tile(B, lc.tile);
   const Tiling t = tiling_of(tv);
   MlpArgs m{x, wg, wu, wd, reinterpret_cast<uint16_t*>(lc.ws + p->off_aux), y, B,
             p->hidden, p->inter, 0};

@@ -27,6 +27,8 @@
 // inline.  Static mode keeps the fine-grained EV_H edge but, as the page's
 // static lowering does for data-dependent edges, replaces EV_EXP by one
 // coarse "all grouped" event and EV_C by one "all down tiles done" event.
+#include <type_traits>
+
 #include "et_device.hpp"
 #include "et_gemm.hpp"
 #include "et_launch.hpp"
@@ -56,7 +58,6 @@ struct MoeArgs {
   int ev_exp, ev_h, ev_c;
 };
 
-template <int MT> constexpr int kMoePD = MT == 1 ? 4 : (MT == 2 ? 3 : 2);   // K-blocks in flight
 constexpr int kMoeSmem = 16384 * 4 + 3 * 1024 * 4 + 256;   // scan histogram + scan temps
 
 // ---------------------------------------------------------------------------
@@ -94,111 +95,204 @@ __device__ int block_exscan(int* a, int n, int* tmp /* >= 8 ints */) {
   return total;
 }
 
-// float -> key that orders like the value (with -0.0 == +0.0), then by lower index
-__device__ __forceinline__ unsigned long long route_key(float v, int e) {
+// float -> unsigned key with the same order (-0.0 and +0.0 map to one key);
+// every finite value maps above 0
+__device__ __forceinline__ uint32_t route_key32(float v) {
   if (v == 0.0f) v = 0.0f;
-  uint32_t u = __builtin_bit_cast(uint32_t, v);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((unsigned long long)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ float key_value(unsigned long long key) {
-  uint32_t u = (uint32_t)(key >> 32);
-  u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
   return __builtin_bit_cast(float, u);
 }
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, d), hi = __shfl_xor((uint32_t)(v >> 32), d);
-    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+
+// Tile variant traits: rows per block, columns per gate/up and down task,
+// and the GEMM tile type of each projection.
+template <int TV>
+struct MoeCfg {
+  static constexpr Tiling t = tiling_of(TV);
+  static constexpr int MT = t.mt;
+  static constexpr bool kWide = TV == TV_W64 || TV == TV_W128;
+  static constexpr int NH = kWide ? 2 : 1;          // 16-column h groups per wave (gate/up)
+  static constexpr int NB2 = kWide ? 4 : 1;         // 16-column groups per wave (down)
+  static constexpr int PD = MT == 1 ? 4 : (MT == 2 ? 3 : 2);
+};
+
+template <int TV, bool COH, int NB>
+struct TileOf {
+  using type = typename std::conditional<
+      MoeCfg<TV>::kWide, RingTile<MoeCfg<TV>::MT, COH>,
+      StreamTile<MoeCfg<TV>::MT, NB, 4, MoeCfg<TV>::PD, COH>>::type;
+};
+
+constexpr int kIdxCache = 2 * (kMaxExperts + 1) * 4;   // tok_indptr + blk_indptr copies
+
+template <class Tile>
+constexpr int smem_bytes() {
+  return (1024 + Tile::kLdsBytes > kMoeSmem ? 1024 + Tile::kLdsBytes : kMoeSmem) + kIdxCache;
 }
 
-// one output element of the combine; the same fixed-order sum serves the
-// inline (dynamic) and the tiled (static) combine, so both give the same bits
-__device__ __forceinline__ float combine_elem(const MoeArgs& m, int t, int col) {
-  float acc = 0.f;
-  for (int s = 0; s < m.k; ++s) {
-    const float w = m.topk_w[t * m.k + s];
-    const int pos = m.inv[t * m.k + s];
-    acc = __fmaf_rn(w, m.y[(size_t)pos * m.H + col], acc);
-  }
-  return acc;
+// Static schedule position of workgroup w: workgroups are dispatched to the
+// XCDs round-robin (w % 8), so positions p*32 .. p*32+31 -- consecutive task
+// ids -- all run on XCD p and share its L2.
+__device__ __forceinline__ int xcd_pos(int w, int G) {
+  return (G % 8 == 0) ? (w % 8) * (G / 8) + w / 8 : w;
 }
 
-template <int MT>
+template <int TV>
 __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m) {
+  using Cfg = MoeCfg<TV>;
+  using Tile1 = typename TileOf<TV, false, 2 * Cfg::NH>::type;   // gate/up: reads x
+  using Tile2 = typename TileOf<TV, true, Cfg::NB2>::type;       // down: reads h (this launch)
+  constexpr int MT = Cfg::MT;
+  constexpr bool kWide = Cfg::kWide;
+  constexpr int bn1 = Cfg::t.bn1, bn2 = Cfg::t.bn2;
   __shared__ Shared sh;
-  __shared__ __align__(16) unsigned char smem[kMoeSmem];
-  using Tile1 = StreamTile<MT, 2, 4, kMoePD<MT>>;
-  using Tile2 = StreamTile<MT, 1, 4, kMoePD<MT>>;
+  __shared__ __align__(16) unsigned char smem[smem_bytes<Tile1>()];
 
   Ctx c;
   if (!prologue(c, ra, &sh)) return;
   const int sched = ra.sched;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rows = 16 * MT;
-  const int nt1 = m.I / 16, nt2 = m.H / 16;
+  const int nt1 = m.I / bn1, nt2 = m.H / bn2;
   const int NR = m.NR;
   const int base1 = 2 * NR + 1;
-  const int wc = m.k * 1;   // EV_C wait count: k rows of a token per column tile
+  const int wc = m.k;   // EV_C wait count: the k rows of a token, one per down column tile
 
   // LDS carve-outs (task kinds never overlap in time inside one workgroup)
   int* s_i = reinterpret_cast<int*>(smem);
   uint32_t* rows_off = reinterpret_cast<uint32_t*>(smem);            // gemm: [16*MT]
-  float* red = reinterpret_cast<float*>(smem + 1024);                 // gemm: reduction
-  int* fired = reinterpret_cast<int*>(smem + 1024 - 256);             // gemm2: fired tokens
+  int* fired = reinterpret_cast<int*>(smem + 512);                    // gemm2: fired tokens
+  void* tscratch = smem + 1024;                                       // gemm: tile LDS
 
   auto meta = [&](int i) { return ld_rlx(&ra.hdr[HDR_META + i]); };
+  // LDS copies of the per-expert row and block offsets (filled once per call
+  // per workgroup, after the scan), so task decoding costs no memory trips
+  int* c_tok = reinterpret_cast<int*>(smem + sizeof(smem) - kIdxCache);
+  int* c_blk = c_tok + kMaxExperts + 1;
+  bool cached = false;
+  auto load_cache = [&]() {
+    if (cached) return;
+    for (int e = tid; e <= m.E; e += kThreads) {
+      c_tok[e] = ld_coh(&m.tok_indptr[e]);
+      c_blk[e] = ld_coh(&m.blk_indptr[e]);
+    }
+    __syncthreads();
+    cached = true;
+  };
+  // task -> (expert, column tile, block): expert e owns nblk_e * nt tasks,
+  // ordered column tile first, then block, so consecutive tasks share a
+  // weight slice; e is the largest expert whose first task is <= t (experts
+  // without rows own no tasks and share their successor's start)
+  auto decode = [&](int t, int nt, int& e, int& n, int& gb) {
+    int lo = 0, hi = m.E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (c_blk[mid] * nt <= t) lo = mid; else hi = mid;
+    }
+    e = lo;
+    const int nblk = c_blk[e + 1] - c_blk[e];
+    const int l = t - c_blk[e] * nt;
+    n = l / nblk;
+    gb = c_blk[e] + l % nblk;
+  };
+  const Rsrc ry = make_rsrc(m.y, (uint32_t)((size_t)m.T * m.k * m.H * 4));
+
+  // Combine for ntok tokens (token of list entry i: tok_of(i)) over columns
+  // [c0, c0 + ncols): out[t, col] = sum_{s<k} w[t, s] * y[inv[t, s], col],
+  // accumulated in slot order with one fused multiply-add per slot.  The
+  // (w, position) pairs are staged in LDS first; each thread then owns 4
+  // columns and issues its k 16-byte row loads before summing, so a pass
+  // costs two memory round trips.  The dynamic (inline) and tiled (static)
+  // combines share this code and give bit-identical results.
+  auto combine = [&](int ntok, auto tok_of, int c0, int ncols, float* cw, int* cp) {
+    const int k = m.k;
+    for (int i = tid; i < ntok * k; i += kThreads) {
+      const int t = tok_of(i / k), s = i % k;
+      cw[i] = ld_coh(&m.topk_w[t * k + s]);
+      cp[i] = ld_coh(&m.inv[t * k + s]);
+    }
+    __syncthreads();
+    const int nq = ncols / 4;              // 4 columns (16 bytes) per item
+    for (int i = tid; i < ntok * nq; i += kThreads) {
+      const int ti = i / nq, col = c0 + 4 * (i % nq);
+      i32x4 yv[kMaxTopK];
+#pragma unroll
+      for (int s = 0; s < kMaxTopK; ++s)
+        if (s < k) yv[s] = ld16c(ry, (uint32_t)((cp[ti * k + s] * (size_t)m.H + col) * 4));
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int s = 0; s < kMaxTopK; ++s)
+        if (s < k) {
+          const float w = cw[ti * k + s];
+          const f32x4 y4 = __builtin_bit_cast(f32x4, yv[s]);
+          acc.x = __fmaf_rn(w, y4[0], acc.x);
+          acc.y = __fmaf_rn(w, y4[1], acc.y);
+          acc.z = __fmaf_rn(w, y4[2], acc.z);
+          acc.w = __fmaf_rn(w, y4[3], acc.w);
+        }
+      *reinterpret_cast<float4*>(m.out + (size_t)tok_of(ti) * m.H + col) = acc;
+    }
+    __syncthreads();
+  };
+  // static / barrier: coarse events already seen fired by this workgroup
+  bool seen_group = false, seen_g1 = false, seen_down = false;
 
   // ------------------------------------------------------------- routing
+  // One wave per token.  Lane l holds the order-preserving integer keys of
+  // experts l, l + 64, ...; each of the k rounds takes the wave-wide largest
+  // key, then the lowest expert index holding it (ties go to the lower index;
+  // -0.0 and +0.0 share a key), with two DPP reductions and no LDS traffic.
   auto route = [&](int r) {
     int* hist_l = s_i;   // [E]
     for (int e = tid; e < m.E; e += kThreads) hist_l[e] = 0;
     __syncthreads();
     const int t0 = r * m.tpr;
     const int t1 = min(m.T, t0 + m.tpr);
+    const int nj = (m.E + 63) / 64;
     for (int t = t0 + wave; t < t1; t += 4) {
       const float* lg = m.logits + (size_t)t * m.E;
-      unsigned long long keys[kMaxExperts / 64];
-      const int nj = (m.E + 63) / 64;
+      uint32_t keys[kMaxExperts / 64];
 #pragma unroll
       for (int j = 0; j < kMaxExperts / 64; ++j) {
         const int e = lane + 64 * j;
-        keys[j] = (j < nj && e < m.E) ? route_key(lg[e], e) : 0ull;
+        keys[j] = (j < nj && e < m.E) ? route_key32(lg[e]) : 0u;   // 0: below every key
       }
+      uint32_t taken = 0;                  // bit j: my expert lane + 64 j already chosen
       int my_e = -1;
-      float my_v = 0.f, v0 = 0.f;
+      uint32_t my_key = 0, key0 = 0;
       for (int s = 0; s < m.k; ++s) {
-        unsigned long long best = 0;
+        uint32_t best = 0;
+        int best_e = 0x7fffffff;
 #pragma unroll
-        for (int j = 0; j < kMaxExperts / 64; ++j) best = keys[j] > best ? keys[j] : best;
-        best = wave_max_u64(best);
-        const int e = (int)(0xffffffffu - (uint32_t)best);
-        const float v = key_value(best);
-        if (s == 0) v0 = v;
-        if (lane == s) { my_e = e; my_v = v; }
-        if ((e & 63) == lane) {
-#pragma unroll
-          for (int j = 0; j < kMaxExperts / 64; ++j)
-            if (j == (e >> 6)) keys[j] = 0ull;
+        for (int j = 0; j < kMaxExperts / 64; ++j) {
+          const bool ok = j < nj && !((taken >> j) & 1u) && lane + 64 * j < m.E;
+          if (ok && keys[j] > best) {   // strict: equal keys keep the lower expert
+            best = keys[j];
+            best_e = lane + 64 * j;
+          }
         }
+        const uint32_t top = wave_reduce_u32<true>(best);
+        const int e = (int)wave_reduce_u32<false>(best == top ? (uint32_t)best_e : 0xffffffffu);
+        if (s == 0) key0 = top;
+        if (lane == s) { my_e = e; my_key = top; }
+        if ((e & 63) == lane) taken |= 1u << (e >> 6);
       }
       // weights: softmax over the kept logits (= renormalised top-k softmax)
-      float ex = lane < m.k ? expf(my_v - v0) : 0.f;
+      const float ex = lane < m.k ? expf(key_to_float(my_key) - key_to_float(key0)) : 0.f;
       float sum = ex;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) sum += __shfl_xor(sum, d);
       if (lane < m.k) {
-        m.topk_ids[t * m.k + lane] = my_e;
-        m.topk_w[t * m.k + lane] = ex / sum;
+        st_coh(&m.topk_ids[t * m.k + lane], my_e);
+        st_coh(&m.topk_w[t * m.k + lane], ex / sum);
         atomicAdd(&hist_l[my_e], 1);
       }
     }
     __syncthreads();
-    for (int e = tid; e < m.E; e += kThreads) m.hist[r * m.E + e] = hist_l[e];
+    for (int e = tid; e < m.E; e += kThreads) st_coh(&m.hist[r * m.E + e], hist_l[e]);
   };
 
   // ------------------------------------------------------------- scan
@@ -207,43 +301,64 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
     int* cnt = s_i + 16384;                // [E]
     int* blk = cnt + 1024;                 // [E] -> block offsets
     int* tmp = blk + 1024;                 // [8]
+    int* part = tmp + 8;                   // [256] chunk sums
     const int n_ne = cdiv(m.T, m.tpr);
     const int tot = n_ne * m.E;
-    for (int i = tid; i < tot; i += kThreads) hs[i] = m.hist[i];
+    // all histogram loads in flight at once (16 per thread per pass)
+    for (int b0 = 0; b0 < tot; b0 += 16 * kThreads) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int i = b0 + u * kThreads + tid;
+        v[u] = i < tot ? ld_coh(&m.hist[i]) : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int i = b0 + u * kThreads + tid;
+        if (i < tot) hs[i] = v[u];
+      }
+    }
     __syncthreads();
-    for (int e = tid; e < m.E; e += kThreads) {
+    // per-expert prefix over the chunks r: P threads per expert, each summing
+    // a contiguous range of r, then the P partial sums in order
+    const int P = m.E >= kThreads ? 1 : kThreads / m.E;
+    const int span = cdiv(n_ne, P);
+    for (int q = tid; q < m.E * P; q += kThreads) {
+      const int e = q / P, p = q % P;
+      int acc = 0;
+      for (int r = p * span; r < min(n_ne, (p + 1) * span); ++r) acc += hs[r * m.E + e];
+      part[q % kThreads] = acc;
+    }
+    __syncthreads();
+    for (int q = tid; q < m.E * P; q += kThreads) {
+      const int e = q / P, p = q % P;
       int run = 0;
-      for (int r = 0; r < n_ne; ++r) {
+      for (int pp = 0; pp < p; ++pp) run += part[(e * P + pp) % kThreads];
+      for (int r = p * span; r < min(n_ne, (p + 1) * span); ++r) {
         const int v = hs[r * m.E + e];
         hs[r * m.E + e] = run;
         run += v;
       }
-      cnt[e] = run;
-      blk[e] = cdiv(run, rows);
-      m.counts[e] = run;
+      if (p == P - 1) {
+        cnt[e] = run;
+        blk[e] = cdiv(run, rows);
+        st_coh(&m.counts[e], run);
+      }
     }
     __syncthreads();
     block_exscan(cnt, m.E, tmp);           // cnt -> tok_indptr
     const int nb = block_exscan(blk, m.E, tmp);
     for (int e = tid; e < m.E; e += kThreads) {
-      m.tok_indptr[e] = cnt[e];
-      m.blk_indptr[e] = blk[e];
-      m.task_indptr[e] = blk[e] * nt1;
+      st_coh(&m.tok_indptr[e], cnt[e]);
+      st_coh(&m.blk_indptr[e], blk[e]);
+      st_coh(&m.task_indptr[e], blk[e] * nt1);
     }
     if (tid == 0) {
-      m.tok_indptr[m.E] = m.T * m.k;
-      m.blk_indptr[m.E] = nb;
-      m.task_indptr[m.E] = nb * nt1;
+      st_coh(&m.tok_indptr[m.E], m.T * m.k);
+      st_coh(&m.blk_indptr[m.E], nb);
+      st_coh(&m.task_indptr[m.E], nb * nt1);
     }
-    for (int i = tid; i < tot; i += kThreads) m.hist[i] = hs[i] + cnt[i % m.E];
-    for (int gb = tid; gb < nb; gb += kThreads) {   // block -> expert (upper bound search)
-      int lo = 0, hi = m.E;                         // blk[lo] <= gb < blk[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (blk[mid] <= gb) lo = mid; else hi = mid;
-      }
-      m.blk_expert[gb] = lo;
-    }
+    for (int i = tid; i < tot; i += kThreads) st_coh(&m.hist[i], hs[i] + cnt[i % m.E]);
     if (tid == 0) {
       st_rlx(&ra.hdr[HDR_META + MD_NB], nb);
       st_rlx(&ra.hdr[HDR_META + MD_TOTAL1], nb * nt1);
@@ -258,7 +373,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
     int* cur = s_i;            // [E] next position per expert
     int* base = s_i + 1024;    // [E] first position of this chunk per expert
     for (int e = tid; e < m.E; e += kThreads) {
-      const int b = m.hist[r * m.E + e];
+      const int b = ld_coh(&m.hist[r * m.E + e]);
       cur[e] = b;
       base[e] = b;
     }
@@ -268,10 +383,10 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
     if (wave == 0) {
       for (int t = t0; t < t1; ++t) {      // tokens in order: stable positions
         if (lane < m.k) {
-          const int e = m.topk_ids[t * m.k + lane];
+          const int e = ld_coh(&m.topk_ids[t * m.k + lane]);
           const int pos = cur[e]++;        // a token's k experts are distinct
-          m.perm[pos] = t * m.k + lane;
-          m.inv[t * m.k + lane] = pos;
+          st_coh(&m.perm[pos], t * m.k + lane);
+          st_coh(&m.inv[t * m.k + lane], pos);
         }
       }
     }
@@ -279,68 +394,108 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
   };
 
   // ------------------------------------------------------------- gemm tiles
+  auto block_rows = [&](int gb, int e, int& pos0, int& pend) {
+    pos0 = c_tok[e] + (gb - c_blk[e]) * rows;
+    pend = min(pos0 + rows, c_tok[e + 1]);
+  };
+
   auto gemm1 = [&](int t1g, int task) -> bool {
-    const int gb = t1g / nt1, n = t1g % nt1;
-    const int e = m.blk_expert[gb];
-    const int pos0 = m.tok_indptr[e] + (gb - m.blk_indptr[e]) * rows;
-    const int pend = min(pos0 + rows, m.tok_indptr[e + 1]);
+    load_cache();
+    int e, n, gb, pos0, pend;
+    decode(t1g, nt1, e, n, gb);
+    block_rows(gb, e, pos0, pend);
     const size_t wofs = (size_t)e * m.I * m.H;
     const uint32_t wbytes = (uint32_t)m.I * m.H * 2;
-    const Rsrc rb[2] = {make_rsrc(m.wg + wofs, wbytes), make_rsrc(m.wu + wofs, wbytes)};
-    const uint32_t boff = (uint32_t)(16 * n + (lane & 15)) * (uint32_t)(m.H * 2);
-    const uint32_t bo[2] = {boff, boff};
+    const Rsrc rgate = make_rsrc(m.wg + wofs, wbytes), rup = make_rsrc(m.wu + wofs, wbytes);
+    const int cw = kWide ? 16 * Cfg::NH * wave : 0;      // this wave's first h column
+    // B rows (output columns) of this wave's groups: gate groups 0..NH-1,
+    // then the up groups for the same h columns.  The stream tile takes each
+    // lane's own row; the ring tile takes the first row of each group.
+    const int lrow = kWide ? 0 : (lane & 15);
+    Rsrc rb[2 * Cfg::NH];
+    uint32_t bo[2 * Cfg::NH];
+#pragma unroll
+    for (int j = 0; j < Cfg::NH; ++j) {
+      const uint32_t off = (uint32_t)(n * bn1 + cw + 16 * j + lrow) * (uint32_t)(m.H * 2);
+      rb[j] = rgate;
+      rb[Cfg::NH + j] = rup;
+      bo[j] = off;
+      bo[Cfg::NH + j] = off;
+    }
     const Rsrc rx = make_rsrc(m.x, (uint32_t)m.T * m.H * 2);
     auto gate = [&](int round) -> bool {
       if (round != 0) return true;
-      if (sched == ET_SCHED_STATIC || sched == ET_SCHED_BARRIER)
+      if ((sched == ET_SCHED_STATIC || sched == ET_SCHED_BARRIER) && !seen_group) {
         if (!wg_wait(c, EV_GROUP, NR, task)) return false;
+        seen_group = true;
+      }
       for (int i = tid; i < rows; i += kThreads) {
         const int pos = pos0 + i;
-        rows_off[i] = pos < pend ? (uint32_t)(m.perm[pos] / m.k) * (uint32_t)(m.H * 2) : kOOB;
+        rows_off[i] = pos < pend ? (uint32_t)(ld_coh(&m.perm[pos]) / m.k) * (uint32_t)(m.H * 2) : kOOB;
       }
       __syncthreads();
       return true;
     };
     Tile1 tile;
-    if (!tile.run(rx, rows_off, rb, bo, m.H / kKBlock, gate, red)) return false;
+    bool ok;
+    if constexpr (kWide)
+      ok = tile.run(rx, rows_off, rb, bo, (uint32_t)(m.H * 2), m.H, gate,
+                    static_cast<unsigned char*>(tscratch));
+    else
+      ok = tile.run(rx, rows_off, rb, bo, m.H / kKBlock, gate, static_cast<float*>(tscratch));
+    if (!ok) return false;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (r == wave) {
-          const int pos = pos0 + 16 * mt + 4 * (lane >> 4) + r;
-          if (pos < pend) {
-            const float g = tile.acc[mt][0][r], u = tile.acc[mt][1][r];
-            m.h[(size_t)pos * m.I + 16 * n + (lane & 15)] = f32_to_bf16(silu(g) * u);
+      for (int j = 0; j < Cfg::NH; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kWide || r == wave) {
+            const int pos = pos0 + 16 * mt + 4 * (lane >> 4) + r;
+            if (pos < pend) {
+              const float g = tile.acc[mt][j][r], u = tile.acc[mt][Cfg::NH + j][r];
+              st_coh(&m.h[(size_t)pos * m.I + n * bn1 + cw + 16 * j + (lane & 15)],
+                     f32_to_bf16(silu(g) * u));
+            }
           }
-        }
     if (sched == ET_SCHED_PER_OP) return true;
     wg_release();
     if (sched == ET_SCHED_BARRIER) {
       t0_notify(c, EV_G1ALL, 1, meta(MD_TOTAL1), task);
     } else if (sched == ET_SCHED_STATIC) {
       t0_notify(c, m.ev_h + gb, 1, nt1, task);
-    } else if (wg_notify(c, m.ev_h + gb, 1, nt1, task, true)) {
-      const int b2 = base1 + meta(MD_TOTAL1) + gb * nt2;
-      wg_push(c, nt2, [&](int i) { return b2 + i; });
+    } else if (wg_notify(c, m.ev_h + gb, 1, nt1, task)) {
+      // block gb's down tasks: expert e's range, one per column tile
+      const int nblk = c_blk[e + 1] - c_blk[e];
+      const int b2 = base1 + meta(MD_TOTAL1) + c_blk[e] * nt2 + (gb - c_blk[e]);
+      wg_push(c, nt2, [&](int i) { return b2 + i * nblk; });
     }
     return true;
   };
 
   auto gemm2 = [&](int t2g, int task) -> bool {
-    const int gb = t2g / nt2, n2 = t2g % nt2;
-    const int e = m.blk_expert[gb];
-    const int pos0 = m.tok_indptr[e] + (gb - m.blk_indptr[e]) * rows;
-    const int pend = min(pos0 + rows, m.tok_indptr[e + 1]);
-    const Rsrc rb[1] = {make_rsrc(m.wd + (size_t)e * m.H * m.I, (uint32_t)m.H * m.I * 2)};
-    const uint32_t bo[1] = {(uint32_t)(16 * n2 + (lane & 15)) * (uint32_t)(m.I * 2)};
+    load_cache();
+    int e, n2, gb, pos0, pend;
+    decode(t2g, nt2, e, n2, gb);
+    block_rows(gb, e, pos0, pend);
+    const Rsrc rdown = make_rsrc(m.wd + (size_t)e * m.H * m.I, (uint32_t)m.H * m.I * 2);
+    const int cw = kWide ? 16 * Cfg::NB2 * wave : 0;     // this wave's first output column
+    const int lrow = kWide ? 0 : (lane & 15);
+    Rsrc rb[Cfg::NB2];
+    uint32_t bo[Cfg::NB2];
+#pragma unroll
+    for (int j = 0; j < Cfg::NB2; ++j) {
+      rb[j] = rdown;
+      bo[j] = (uint32_t)(n2 * bn2 + cw + 16 * j + lrow) * (uint32_t)(m.I * 2);
+    }
     const Rsrc rh = make_rsrc(m.h, (uint32_t)m.T * m.k * m.I * 2);
     auto gate = [&](int round) -> bool {
       if (round != 0) return true;
       if (sched == ET_SCHED_STATIC) {
         if (!wg_wait(c, m.ev_h + gb, nt1, task)) return false;
-      } else if (sched == ET_SCHED_BARRIER) {
+      } else if (sched == ET_SCHED_BARRIER && !seen_g1) {
         if (!wg_wait(c, EV_G1ALL, meta(MD_TOTAL1), task)) return false;
+        seen_g1 = true;
       }
       for (int i = tid; i < rows; i += kThreads) {
         const int pos = pos0 + i;
@@ -350,15 +505,24 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
       return true;
     };
     Tile2 tile;
-    if (!tile.run(rh, rows_off, rb, bo, m.I / kKBlock, gate, red)) return false;
+    bool ok;
+    if constexpr (kWide)
+      ok = tile.run(rh, rows_off, rb, bo, (uint32_t)(m.I * 2), m.I, gate,
+                    static_cast<unsigned char*>(tscratch));
+    else
+      ok = tile.run(rh, rows_off, rb, bo, m.I / kKBlock, gate, static_cast<float*>(tscratch));
+    if (!ok) return false;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (r == wave) {
-          const int pos = pos0 + 16 * mt + 4 * (lane >> 4) + r;
-          if (pos < pend) m.y[(size_t)pos * m.H + 16 * n2 + (lane & 15)] = tile.acc[mt][0][r];
-        }
+      for (int j = 0; j < Cfg::NB2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kWide || r == wave) {
+            const int pos = pos0 + 16 * mt + 4 * (lane >> 4) + r;
+            if (pos < pend)
+              st_coh(&m.y[(size_t)pos * m.H + n2 * bn2 + cw + 16 * j + (lane & 15)], tile.acc[mt][j][r]);
+          }
     if (sched == ET_SCHED_PER_OP) return true;
     wg_release();
     if (sched != ET_SCHED_DYNAMIC) {
@@ -371,37 +535,33 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
     if (tid < rows) {
       const int pos = pos0 + tid;
       if (pos < pend) {
-        const int t = m.perm[pos] / m.k;
+        const int t = ld_coh(&m.perm[pos]) / m.k;
         const int idx = m.ev_c + t * nt2 + n2;
-        const int old = add_acqrel(c.ev + idx, -1);
+        const int old = add_rlx(c.ev + idx, -1);
         if (old - 1 == -wc) fired[atomicAdd(&sh.v[5], 1)] = t;
         else if (old - 1 < -wc) raise_fault(ra, ET_ESTATE, task, idx, old - 1);
       }
     }
     __syncthreads();
     const int nf = sh.v[5];
-    if (nf > 0) {
-      fence_acquire();
-      for (int i = tid; i < nf * 16; i += kThreads) {
-        const int t = fired[i >> 4];
-        const int col = 16 * n2 + (i & 15);
-        m.out[(size_t)t * m.H + col] = combine_elem(m, t, col);
-      }
-    }
-    __syncthreads();
+    if (nf > 0)
+      combine(nf, [&](int i) { return fired[i]; }, n2 * bn2, bn2,
+              reinterpret_cast<float*>(tscratch), reinterpret_cast<int*>(tscratch) + kMaxTopK * 128);
     return true;
   };
 
   auto combine_tile = [&](int t3, int task) -> bool {
-    if (sched == ET_SCHED_STATIC || sched == ET_SCHED_BARRIER)
+    if ((sched == ET_SCHED_STATIC || sched == ET_SCHED_BARRIER) && !seen_down) {
       if (!wg_wait(c, EV_DOWN, meta(MD_TOTAL2), task)) return false;
+      seen_down = true;
+    }
     const int ncol = cdiv(m.H, kCombCols);
     const int tc = t3 / ncol, cc = t3 % ncol;
-    const int col = cc * kCombCols + tid;
-    if (col < m.H) {
-      const int te = min(m.T, (tc + 1) * kCombTok);
-      for (int t = tc * kCombTok; t < te; ++t) m.out[(size_t)t * m.H + col] = combine_elem(m, t, col);
-    }
+    const int t0 = tc * kCombTok;
+    const int ntok = min(m.T, t0 + kCombTok) - t0;
+    const int c0 = cc * kCombCols;
+    combine(ntok, [&](int i) { return t0 + i; }, c0, min(kCombCols, m.H - c0),
+            reinterpret_cast<float*>(tscratch), reinterpret_cast<int*>(tscratch) + kMaxTopK * 128);
     return true;
   };
 
@@ -413,7 +573,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
       wg_release();
       if (sched != ET_SCHED_DYNAMIC) {
         t0_notify(c, EV_ROUTE, 1, NR, task);
-      } else if (wg_notify(c, EV_ROUTE, 1, NR, task, true)) {
+      } else if (wg_notify(c, EV_ROUTE, 1, NR, task)) {
         wg_push(c, 1, [&](int) { return NR; });          // the scan task
       }
       return true;
@@ -454,18 +614,17 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
       for (int e = tid; e < m.E; e += kThreads) {
         const int n = cur[e] - base[e];
         if (n > 0) {
-          const int wcnt = m.counts[e];
-          const int old = add_acqrel(c.ev + m.ev_exp + e, -n);
+          const int wcnt = ld_coh(&m.counts[e]);
+          const int old = add_rlx(c.ev + m.ev_exp + e, -n);
           if (old - n == -wcnt) fe[atomicAdd(&sh.v[6], 1)] = e;
           else if (old - n < -wcnt) raise_fault(ra, ET_ESTATE, task, m.ev_exp + e, old - n);
         }
       }
       __syncthreads();
       const int nf = sh.v[6];
-      if (nf > 0) fence_acquire();
       for (int i = 0; i < nf; ++i) {
         const int e = fe[i];
-        const int lo = m.task_indptr[e], hi = m.task_indptr[e + 1];
+        const int lo = ld_coh(&m.task_indptr[e]), hi = ld_coh(&m.task_indptr[e + 1]);
         wg_push(c, hi - lo, [&](int j) { return base1 + lo + j; });
       }
       __syncthreads();
@@ -478,13 +637,14 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
   };
 
   const int ncomb = cdiv(m.T, kCombTok) * cdiv(m.H, kCombCols);
-  int tasks_run = 0;
   if (sched == ET_SCHED_DYNAMIC) {
     PopState ps;
     for (;;) {
       const int t = wg_pop(c, ps);
+      const long long t0 = trace_now(c);
       if (t < 0 || !run(t)) break;
       count_run(c, t);
+      trace_task(c, t, t0);
     }
   } else if (sched == ET_SCHED_PER_OP) {
     const int ph = ra.phase;
@@ -498,35 +658,44 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
       else if (ph == 4) { lo = base1 + total1; hi = lo + total2; }
       else { lo = base1 + total1 + total2; hi = lo + ncomb; }
     }
-    for (int t = lo + c.wg; t < hi; t += c.G) {
+    for (int t = lo + (ph >= 3 ? xcd_pos(c.wg, c.G) : c.wg); t < hi; t += c.G) {
+      const long long t0 = trace_now(c);
       run(t);
       count_run(c, t);
+      trace_task(c, t, t0);
     }
   } else {
     bool ok = true;
     for (int t = c.wg; ok && t < NR; t += c.G) {
+      const long long t0 = trace_now(c);
       ok = run(t);
       if (ok) count_run(c, t);
+      if (ok) trace_task(c, t, t0);
     }
     if (ok && c.wg == c.G - 1) {
+      const long long t0 = trace_now(c);
       ok = run(NR);
       if (ok) count_run(c, NR);
+      if (ok) trace_task(c, NR, t0);
     }
     for (int r = c.wg; ok && r < NR; r += c.G) {
+      const long long t0 = trace_now(c);
       ok = run(NR + 1 + r);
       if (ok) count_run(c, NR + 1 + r);
+      if (ok) trace_task(c, NR + 1 + r, t0);
     }
     if (ok) ok = wg_wait(c, EV_SCAN, 1, -1);
     if (ok) {
       const int total1 = meta(MD_TOTAL1), total2 = meta(MD_TOTAL2);
       const int end = base1 + total1 + total2 + ncomb;
-      for (int t = base1 + c.wg; ok && t < end; t += c.G) {
+      for (int t = base1 + xcd_pos(c.wg, c.G); ok && t < end; t += c.G) {
+        const long long t0 = trace_now(c);
         ok = run(t);
         if (ok) count_run(c, t);
+        if (ok) trace_task(c, t, t0);
       }
     }
   }
-  (void)tasks_run;
   epilogue(c, 0);
 }
 
@@ -537,7 +706,7 @@ int launch_moe(const LaunchCommon& lc, const float* logits, const uint16_t* x, i
              moe_n_route(p->n_experts)};
   const MoeAux ax = moe_aux_layout(mp);
   char* aux = lc.ws + p->off_aux;
-  const int tv = pick_tile(T, lc.tile);
+  const int tv = pick_moe_tile(T, p->top_k, p->n_experts, lc.tile);
   const Tiling tl = tiling_of(tv);
   MoeArgs m;
   m.logits = logits;
@@ -570,11 +739,16 @@ int launch_moe(const LaunchCommon& lc, const float* logits, const uint16_t* x, i
   m.ev_c = mp.ev_c();
   RunArgs ra = lc.run_args();
   ra.n_init = mp.n_route;
+  ra.n_single = 2 * mp.n_route + 1;   // routing, scan and grouping: one slot per claim
   ra.total_hint = kUnknownTotal;
   ra.extent = mp.extent(T, tl);
-  const void* k = tv == TV_M16   ? reinterpret_cast<const void*>(&moe_kernel<1>)
-                  : tv == TV_M32 ? reinterpret_cast<const void*>(&moe_kernel<2>)
-                                 : reinterpret_cast<const void*>(&moe_kernel<4>);
+  const void* const kernels[TV_COUNT] = {
+      reinterpret_cast<const void*>(&moe_kernel<TV_M16>),
+      reinterpret_cast<const void*>(&moe_kernel<TV_M32>),
+      reinterpret_cast<const void*>(&moe_kernel<TV_M64>),
+      reinterpret_cast<const void*>(&moe_kernel<TV_W64>),
+      reinterpret_cast<const void*>(&moe_kernel<TV_W128>)};
+  const void* k = kernels[tv];
   if (lc.sched == ET_SCHED_PER_OP) {
     for (int ph = 0; ph < 6; ++ph) {
       ra.phase = ph;

@@ -54,15 +54,18 @@ struct Tiling {
   int bn2;   // output columns per down task
 };
 
-// Variant ids (kernels are instantiated per variant).
-enum : int { TV_M16 = 0, TV_M32 = 1, TV_M64 = 2, TV_COUNT = 3 };
+// Variant ids (kernels are instantiated per variant).  The stream variants
+// (16 / 32 / 64 rows, 16-column tasks) serve few rows per expert, where the
+// weight stream from HBM is the bound and many narrow tasks keep every CU
+// busy; the wide variants (64 / 128 rows, 128 h columns per gate/up task and
+// 256 output columns per down task) serve many rows, where MFMA throughput
+// and operand reuse matter.
+enum : int { TV_M16 = 0, TV_M32 = 1, TV_M64 = 2, TV_W64 = 3, TV_W128 = 4, TV_COUNT = 5 };
 
-ET_HD Tiling tiling_of(int tv) {
-  Tiling t;
-  t.mt = tv == TV_M16 ? 1 : (tv == TV_M32 ? 2 : 4);
-  t.bn1 = 16;
-  t.bn2 = 16;
-  return t;
+__host__ __device__ constexpr Tiling tiling_of(int tv) {
+  return Tiling{tv == TV_M16 ? 1 : (tv == TV_M32 ? 2 : (tv == TV_W128 ? 8 : 4)),
+                (tv == TV_W64 || tv == TV_W128) ? 128 : 16,
+                (tv == TV_W64 || tv == TV_W128) ? 256 : 16};
 }
 constexpr int kMinRows = 16;       // smallest rows per tile over all variants
 constexpr int kMinCols = 16;       // smallest bn1 / bn2 over all variants

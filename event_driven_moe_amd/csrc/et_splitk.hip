@@ -30,7 +30,7 @@ __device__ __forceinline__ void splitk_stage1(const SplitKArgs& s, int i, int j)
   v += __shfl_xor(v, 1);
   v += __shfl_xor(v, 2);
   v += __shfl_xor(v, 4);
-  if ((t & 7) == 0) s.B[(size_t)r * 4 + j] = v;
+  if ((t & 7) == 0) st_coh(&s.B[(size_t)r * 4 + j], v);
 }
 
 // Stage-2 tile: C[r] = ((B[r,0] + B[r,1]) + B[r,2]) + B[r,3] for 32 rows.
@@ -38,8 +38,8 @@ __device__ __forceinline__ void splitk_stage2(const SplitKArgs& s, int i) {
   const int t = threadIdx.x;
   if (t < 32) {
     const int r = 32 * i + t;
-    const float4 b = *reinterpret_cast<const float4*>(s.B + (size_t)r * 4);
-    s.C[r] = ((b.x + b.y) + b.z) + b.w;
+    const float* b = s.B + (size_t)r * 4;
+    s.C[r] = ((ld_coh(b) + ld_coh(b + 1)) + ld_coh(b + 2)) + ld_coh(b + 3);
   }
 }
 
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kThreads, 1) void splitk_kernel(RunArgs ra, SplitKA
         t0_notify(c, ev_all, 1, n1, task);
       } else if (sched == ET_SCHED_STATIC) {
         t0_notify(c, i, 1, 4, task);
-      } else if (wg_notify(c, i, 1, 4, task, true)) {
+      } else if (wg_notify(c, i, 1, 4, task)) {
         wg_push(c, 1, [&](int) { return n1 + i; });   // the zeroing notifier pushes stage-2 i
       }
       return true;
@@ -81,24 +81,32 @@ __global__ __launch_bounds__(kThreads, 1) void splitk_kernel(RunArgs ra, SplitKA
     PopState ps;
     for (;;) {
       const int t = wg_pop(c, ps);
+      const long long t0 = trace_now(c);
       if (t < 0 || !run(t)) break;
       count_run(c, t);
+      trace_task(c, t, t0);
     }
   } else if (sched == ET_SCHED_PER_OP) {
     const int lo = ra.phase == 0 ? 0 : n1, hi = ra.phase == 0 ? n1 : total;
     for (int t = lo + c.wg; t < hi; t += c.G) {
+      const long long t0 = trace_now(c);
       run(t);
       count_run(c, t);
+      trace_task(c, t, t0);
     }
   } else {
     bool ok = true;
     for (int t = c.wg; ok && t < n1; t += c.G) {
+      const long long t0 = trace_now(c);
       ok = run(t);
       if (ok) count_run(c, t);
+      if (ok) trace_task(c, t, t0);
     }
     for (int t = n1 + c.wg; ok && t < total; t += c.G) {
+      const long long t0 = trace_now(c);
       ok = run(t);
       if (ok) count_run(c, t);
+      if (ok) trace_task(c, t, t0);
     }
   }
   epilogue(c, total);

@@ -20,7 +20,7 @@ SCHED_STATIC, SCHED_DYNAMIC, SCHED_BARRIER, SCHED_PER_OP = 0, 1, 2, 3
 SCHEDS = {"static": 0, "dynamic": 1, "barrier": 2, "per_op": 3}
 OK, EINVAL, EWORKSPACE, EHIP, ETIMEOUT, EUNSUPPORTED, ESTATE = range(7)
 WL_SPLITK, WL_MLP, WL_MOE = 1, 2, 3
-DEBUG_COUNTS = 1
+DEBUG_COUNTS, DEBUG_TRACE = 1, 2
 
 c_int, c_size_t, c_void_p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 
@@ -34,12 +34,14 @@ class Plan(ctypes.Structure):
     _fields_ = [("workload", c_int), ("max_tokens", c_int), ("hidden", c_int), ("inter", c_int),
                 ("n_experts", c_int), ("top_k", c_int), ("n_events", c_int),
                 ("max_tasks", c_int), ("bytes", c_size_t), ("off_counters", c_size_t),
-                ("off_slots", c_size_t), ("off_runs", c_size_t), ("off_aux", c_size_t),
+                ("off_slots", c_size_t), ("off_runs", c_size_t), ("off_trace", c_size_t),
+                ("off_aux", c_size_t),
                 ("aux_bytes", c_size_t)]
 
 
 class Layout(ctypes.Structure):
     _fields_ = [("counters_bank", c_size_t * 2), ("n_events", c_int), ("runs", c_size_t),
+                ("trace", c_size_t),
                 ("topk_ids", c_size_t), ("topk_w", c_size_t), ("counts", c_size_t),
                 ("tok_indptr", c_size_t), ("perm", c_size_t), ("inv", c_size_t),
                 ("task_indptr", c_size_t), ("h", c_size_t)]
@@ -184,6 +186,14 @@ class Workspace:
     def runs(self):
         lay = self.layout()
         return self.view(lay.runs, torch.int32, self.plan.max_tasks)
+
+    def trace(self):
+        """(tasks [max_tasks, 4]: workgroup, start, end, valid; workgroups [1024, 2]:
+        start, end) in 100 MHz ticks (low 32 bits), from ET_DEBUG_TRACE calls."""
+        lay = self.layout()
+        n = self.plan.max_tasks
+        t = self.view(lay.trace, torch.int32, 4 * n + 2048)
+        return t[:4 * n].view(n, 4), t[4 * n:].view(1024, 2)
 
 
 def splitk_reduce(A, Bpart, C, ws, sched="static", stream=None, **opts):

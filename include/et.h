@@ -73,7 +73,8 @@ enum { ET_WL_SPLITK = 1, ET_WL_MLP = 2, ET_WL_MOE = 3 };
 
 /* Debug flags. */
 enum {
-  ET_DEBUG_COUNTS = 1   /* count how many times each task ran (et_layout.runs) */
+  ET_DEBUG_COUNTS = 1,  /* count how many times each task ran (et_layout.runs) */
+  ET_DEBUG_TRACE = 2    /* record each task's workgroup and start / end time (et_layout.trace) */
 };
 
 /* Per-call options; pass NULL for the defaults. */
@@ -96,6 +97,7 @@ typedef struct et_plan {
   size_t off_counters; /* int32 [2][n_events] event counters (two banks) */
   size_t off_slots;    /* int32 [max_tasks] ready-queue slots */
   size_t off_runs;     /* int32 [max_tasks] per-task run counts (ET_DEBUG_COUNTS) */
+  size_t off_trace;    /* int32 [max_tasks][4] task trace + [1024][2] workgroup times (ET_DEBUG_TRACE) */
   size_t off_aux;      /* workload intermediates (see et_layout) */
   size_t aux_bytes;
 } et_plan;
@@ -106,6 +108,8 @@ typedef struct et_layout {
   size_t counters_bank[2];  /* int32 event counters of each bank */
   int n_events;
   size_t runs;              /* int32 run counts, indexed by task id */
+  size_t trace;             /* int32 [max_tasks][4]: workgroup, start, end (100 MHz ticks,
+                               low 32 bits), 1; then [1024][2] workgroup start / end */
   size_t topk_ids;          /* MoE: int32 [T, k] */
   size_t topk_w;            /* MoE: float [T, k] renormalised routing weights */
   size_t counts;            /* MoE: int32 [E] rows per expert */

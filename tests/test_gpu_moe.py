@@ -73,10 +73,21 @@ def test_modes_bit_identical(name, T):
         assert np.array_equal(o, outs[0])
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2])
-def test_tile_variants(tile):
-    _, _, _, _, out, aux, _ = run_moe("moe_skewed", 64, "dynamic", tile=tile)
-    check_against_oracle("moe_skewed", 64, out, aux)
+def moe_tiling(T, tile=-1):
+    """(rows per block, h columns per gate/up task, columns per down task) of
+    the library's tile variant for T tokens (or the forced variant)."""
+    tv = tile if tile >= 0 else (0 if T <= 16 else 1 if T <= 32 else 2 if T <= 128 else
+                                 3 if T <= 512 else 4)
+    return {0: (16, 16, 16), 1: (32, 16, 16), 2: (64, 16, 16), 3: (64, 128, 256),
+            4: (128, 128, 256)}[tv]
+
+
+@pytest.mark.parametrize("sched", ["static", "dynamic"])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("T", [64, 1024])
+def test_tile_variants(tile, sched, T):
+    _, _, _, _, out, aux, _ = run_moe("moe_skewed", T, sched, tile=tile)
+    check_against_oracle("moe_skewed", T, out, aux)
 
 
 @pytest.mark.parametrize("fetch", [1, 8])
@@ -97,8 +108,8 @@ def test_event_invariants(sched):
     st = ws.status()
     E, k, H, I = cfg["n_experts"], cfg["top_k"], cfg["hidden"], cfg["inter"]
     nr = min(128, 16384 // E)
-    rows = 64          # T = 256 -> 64-row tiles
-    tab = oev.moe_table(aux["counts"], rows, I, 16, H, 16, nr)
+    rows, bn1, bn2 = moe_tiling(T)
+    tab = oev.moe_table(aux["counts"], rows, I, bn1, H, bn2, nr)
     ncomb = -(-T // 16) * -(-H // 256) if sched == "static" else 0
     total = sum(tab["tasks"].values()) + ncomb
     runs = ws.runs().cpu().numpy()
@@ -112,9 +123,9 @@ def test_event_invariants(sched):
         assert (cnt[ev_exp:ev_exp + E] == -tab["events"]["E_exp"]["wait_count"]).all()
         nb_max = -(-1024 * k // 16) + E
         ev_c = ev_h + nb_max
-        assert (cnt[ev_c:ev_c + T * (H // 16)] == -k).all()
+        assert (cnt[ev_c:ev_c + T * (H // bn2)] == -k).all()
     else:
-        assert cnt[1] == -1 and cnt[2] == -nr and cnt[4] == -(nb * (H // 16))
+        assert cnt[1] == -1 and cnt[2] == -nr and cnt[4] == -(nb * (H // bn2))
     check_against_oracle(name, T, out, aux)
 
 
