@@ -300,10 +300,14 @@ __device__ __forceinline__ int wg_pop(const Ctx& c, PopState& ps) {
   int t = -1;
   if (threadIdx.x == 0) {
     if (ps.left == 0) {
-      // short leading phases (few, latency-critical tasks) are claimed one
-      // slot at a time so they spread over all workers; later, `fetch` slots
-      // per atomic (a racy peek is enough: any claim size is correct)
-      const int sz = ld_rlx(&c.a.hdr[HDR_QHEAD]) < c.a.n_single ? 1 : c.a.fetch;
+      // `fetch` slots per atomic only when that many are already published
+      // (pushed or initial) beyond the claim counter: a worker never holds
+      // published tasks while it waits for an unpublished one, and short
+      // leading phases spread over all workers.  A racy peek is enough: any
+      // claim size is correct.
+      const int head = ld_rlx(&c.a.hdr[HDR_QHEAD]);
+      const int avail = c.a.n_init + ld_rlx(&c.a.hdr[HDR_QPUSH]) - head;
+      const int sz = (head < c.a.n_single || avail < c.a.fetch) ? 1 : c.a.fetch;
       ps.base = add_rlx(&c.a.hdr[HDR_QHEAD], sz);
       ps.size = sz;
       ps.left = sz;

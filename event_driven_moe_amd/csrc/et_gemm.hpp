@@ -43,7 +43,8 @@ namespace et {
 template <int MT, int NB, int WK, int PD, bool COH>
 struct StreamTile {
   static constexpr int kRedFloats = WK > 1 ? 4 * MT * NB * 4 * 64 : 1;   // LDS floats
-  static constexpr int kLdsBytes = kRedFloats * 4;
+  static constexpr int kLdsBytes = kRedFloats * 4;   // reduction scratch
+  static constexpr int kStageBytes = 0;                // no LDS ring
 
   // acc[mt][nb]: rows 16*mt + 4*(lane/16) + r, column 16*nb + lane%16 of this
   // wave's column group (for WK > 1: summed over the K-split waves).
@@ -167,8 +168,7 @@ struct RingTile {
   static constexpr int kRows = 16 * MT;                   // A rows
   static constexpr int kCols = 256;                       // B rows = output columns
   static constexpr int kStageBytes = (kRows + kCols) * 128;
-  static constexpr int kStages = 3;
-  static constexpr int kLdsBytes = kStages * kStageBytes;
+  static constexpr int kLdsBytes = 0;                     // besides the three ring slots
   static constexpr int kLA = kRows / 32;                  // A copies per wave per stage
   static constexpr int kLB = 8;                           // B copies per wave per stage
   static constexpr int kL = kLA + kLB;
@@ -177,10 +177,14 @@ struct RingTile {
 
   // rb[n] / b_row0[n]: buffer and byte offset of the first row (output
   // column) of this wave's 16-column group n; rows are b_stride bytes apart.
+  // s0, s1, s2: the three ring slots, three distinct __shared__ arrays of
+  // kStageBytes each -- distinct objects let the compiler wait only for the
+  // copies into the slot being read, so two stages stay in flight.
   template <class Gate>
   __device__ __forceinline__ bool run(Rsrc ra, const uint32_t* a_row_off /* [kRows], LDS */,
                                       const Rsrc* rb, const uint32_t* b_row0, uint32_t b_stride,
-                                      int K, Gate gate, unsigned char* lds /* kLdsBytes */) {
+                                      int K, Gate gate, unsigned char* s0, unsigned char* s1,
+                                      unsigned char* s2) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nks = K / 64;
@@ -199,20 +203,19 @@ struct RingTile {
       const int c = cpos ^ ((j >> 1) & 7);
       boff[q] = b_row0[q >> 1] + (uint32_t)j * b_stride + 16u * c;
     }
-    auto issue_b = [&](int ks) {
-      unsigned char* dst = lds + (ks % kStages) * kStageBytes + kRows * 128 + wave * 64 * 128;
+    auto issue_b = [&](int ks, unsigned char* slot) {
+      unsigned char* dst = slot + kRows * 128 + wave * 64 * 128;
 #pragma unroll
       for (int q = 0; q < kLB; ++q) dma16<false>(rb[q >> 1], dst + q * 1024, boff[q] + ks * 128u);
     };
     uint32_t aoff[kLA];
-    auto issue_a = [&](int ks) {
-      unsigned char* dst = lds + (ks % kStages) * kStageBytes;
+    auto issue_a = [&](int ks, unsigned char* slot) {
 #pragma unroll
-      for (int u = 0; u < kLA; ++u) dma16<COH>(ra, dst + (wave + 4 * u) * 1024, aoff[u] + ks * 128u);
+      for (int u = 0; u < kLA; ++u) dma16<COH>(ra, slot + (wave + 4 * u) * 1024, aoff[u] + ks * 128u);
     };
 
-    issue_b(0);
-    if (nks > 1) issue_b(1);
+    issue_b(0, s0);
+    if (nks > 1) issue_b(1, s1);
     if (!gate(0)) {
       wait_vm_barrier<0>();
       return false;
@@ -223,42 +226,50 @@ struct RingTile {
       const uint32_t base = a_row_off[row];
       aoff[u] = base == kOOB ? kOOB : base + 16u * (uint32_t)(cpos ^ ((row >> 1) & 7));
     }
-    issue_a(0);
-    if (nks > 1) issue_a(1);
+    issue_a(0, s0);
+    if (nks > 1) issue_a(1, s1);
 
     // fragment read offsets: row (lane % 16) of each 16-row group, logical
     // chunk 4s + g -> physical chunk (4s + g) ^ ((lane % 16) / 2 mod 8)
     const int fi = lane & 15, fg = lane >> 4;
     uint32_t foff[2];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-      foff[s2] = (uint32_t)fi * 128u + 16u * (uint32_t)((4 * s2 + fg) ^ ((fi >> 1) & 7));
+    for (int s2i = 0; s2i < 2; ++s2i)
+      foff[s2i] = (uint32_t)fi * 128u + 16u * (uint32_t)((4 * s2i + fg) ^ ((fi >> 1) & 7));
 
-    for (int ks = 0; ks < nks; ++ks) {
+    // one stage: wait for slot `cur` (this wave's copies, then the barrier for
+    // everyone's), refill slot `nxt2` (read two stages ago) with stage ks + 2,
+    // then the MFMAs of stage ks
+    auto step = [&](int ks, const unsigned char* cur, unsigned char* nxt2) {
+      if (ks >= nks) return;
       if (ks == 0 || ks + 1 >= nks)
         wait_vm_barrier<0>();
       else
-        wait_vm_barrier<kL>();      // the stage after this one may still be in flight
+        wait_vm_barrier<kL>();      // stage ks + 1 may still be in flight
       if (ks + 2 < nks) {
-        issue_b(ks + 2);
-        issue_a(ks + 2);
+        issue_b(ks + 2, nxt2);
+        issue_a(ks + 2, nxt2);
       }
-      const unsigned char* st = lds + (ks % kStages) * kStageBytes;
-      const unsigned char* sb = st + kRows * 128 + wave * 64 * 128;
+      const unsigned char* sb = cur + kRows * 128 + wave * 64 * 128;
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
+      for (int s2i = 0; s2i < 2; ++s2i) {
         i32x4 bf[4], af[MT];
 #pragma unroll
         for (int n = 0; n < 4; ++n)
-          bf[n] = *reinterpret_cast<const i32x4*>(sb + n * 16 * 128 + foff[s2]);
+          bf[n] = *reinterpret_cast<const i32x4*>(sb + n * 16 * 128 + foff[s2i]);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-          af[m] = *reinterpret_cast<const i32x4*>(st + m * 16 * 128 + foff[s2]);
+          af[m] = *reinterpret_cast<const i32x4*>(cur + m * 16 * 128 + foff[s2i]);
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
           for (int n = 0; n < 4; ++n) acc[m][n] = mfma16(af[m], bf[n], acc[m][n]);
       }
+    };
+    for (int ks = 0; ks < nks; ks += 3) {
+      step(ks, s0, s2);
+      step(ks + 1, s1, s0);
+      step(ks + 2, s2, s1);
     }
     wait_vm_barrier<0>();            // the ring may be refilled by the next task
     return true;

@@ -52,15 +52,16 @@ inline int pick_mlp_tile(int batch, int forced) {
 }
 
 // MoE: a token count bounds the rows any one expert receives (a token picks
-// an expert at most once); few rows -> narrow stream tiles, many rows -> wide
-// MFMA tiles.  `forced` (0 .. TV_COUNT-1) overrides.
+// an expert at most once); few rows -> narrow stream tiles (their tasks are
+// short, so the weights of a small expert spread over many CUs), many routed
+// rows in total -> wide LDS-staged MFMA tiles (each weight byte feeds more
+// rows).  `forced` (0 .. TV_COUNT-1) overrides.
 inline int pick_moe_tile(int tokens, int top_k, int n_experts, int forced) {
   if (forced >= 0 && forced < TV_COUNT) return forced;
-  (void)top_k;
   (void)n_experts;
   if (tokens <= 16) return TV_M16;
   if (tokens <= 32) return TV_M32;
-  if (tokens <= 128) return TV_M64;
+  if (tokens * top_k <= 256) return TV_M64;
   if (tokens <= 512) return TV_W64;
   return TV_W128;
 }

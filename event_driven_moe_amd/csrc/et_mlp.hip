@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreads, 1) void mlp_kernel(RunArgs ra, MlpArgs m)
   const int total = n_gate + n_down;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  auto set_rows = [&](int b, int row_bytes) {
+  auto set_rows = [&](int b, int row_bytes) ET_INLINE {
     for (int i = threadIdx.x; i < rows; i += kThreads) {
       const int r = b * rows + i;
       rows_off[i] = r < m.B ? (uint32_t)r * (uint32_t)row_bytes : kOOB;
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads, 1) void mlp_kernel(RunArgs ra, MlpArgs m)
     __syncthreads();
   };
 
-  auto run = [&](int task) -> bool {
+  auto run = [&](int task) ET_INLINE -> bool {
     if (task < n_gate) {
       const int b = task / ngt, n = task % ngt;
       set_rows(b, m.H * 2);
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kThreads, 1) void mlp_kernel(RunArgs ra, MlpArgs m)
     const uint32_t bo[1] = {(uint32_t)(16 * n2 + (lane & 15)) * (uint32_t)(m.I * 2)};
     const int nkb = m.I / kKBlock;
     bool ready = sched == ET_SCHED_PER_OP;
-    auto gate = [&](int round) -> bool {
+    auto gate = [&](int round) ET_INLINE -> bool {
       if (ready) return true;
       if (sched == ET_SCHED_BARRIER) return round > 0 || wg_wait(c, m.ev_all, n_gate, task);
       // one round trip checks every h tile of the row block; if some are not

@@ -58,7 +58,13 @@ struct MoeArgs {
   int ev_exp, ev_h, ev_c;
 };
 
-constexpr int kMoeSmem = 16384 * 4 + 3 * 1024 * 4 + 256;   // scan histogram + scan temps
+// LDS: three slot arrays (the GEMM ring of the wide variants; scratch for
+// the other task kinds) and a small general region.
+constexpr int kScanHistBytes = kHistEntries * 4;                    // slot 0
+constexpr int kScanTempBytes = (2 * kMaxExperts + 8 + kThreads) * 4; // slot 1
+constexpr int kGenRowsOff = 0, kGenFired = 512, kGenIdx = 1024;
+constexpr int kIdxCache = 2 * (kMaxExperts + 1) * 4;   // tok_indptr + blk_indptr copies
+constexpr int kGenBytes = kGenIdx + kIdxCache;
 
 // ---------------------------------------------------------------------------
 // block-wide exclusive scan of n <= 1024 ints held in LDS (in place);
@@ -126,12 +132,8 @@ struct TileOf {
       StreamTile<MoeCfg<TV>::MT, NB, 4, MoeCfg<TV>::PD, COH>>::type;
 };
 
-constexpr int kIdxCache = 2 * (kMaxExperts + 1) * 4;   // tok_indptr + blk_indptr copies
-
-template <class Tile>
-constexpr int smem_bytes() {
-  return (1024 + Tile::kLdsBytes > kMoeSmem ? 1024 + Tile::kLdsBytes : kMoeSmem) + kIdxCache;
-}
+template <int A, int B>
+constexpr int cmax() { return A > B ? A : B; }
 
 // Static schedule position of workgroup w: workgroups are dispatched to the
 // XCDs round-robin (w % 8), so positions p*32 .. p*32+31 -- consecutive task
@@ -148,8 +150,12 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
   constexpr int MT = Cfg::MT;
   constexpr bool kWide = Cfg::kWide;
   constexpr int bn1 = Cfg::t.bn1, bn2 = Cfg::t.bn2;
+  constexpr int kSlot = kWide ? Tile1::kStageBytes : 0;
   __shared__ Shared sh;
-  __shared__ __align__(16) unsigned char smem[smem_bytes<Tile1>()];
+  __shared__ __align__(16) unsigned char gen[kGenBytes];
+  __shared__ __align__(16) unsigned char s0[cmax<cmax<kSlot, kScanHistBytes>(), Tile1::kLdsBytes>()];
+  __shared__ __align__(16) unsigned char s1[cmax<kSlot, kScanTempBytes>()];
+  __shared__ __align__(16) unsigned char s2[cmax<kSlot, 16>()];
 
   Ctx c;
   if (!prologue(c, ra, &sh)) return;
@@ -162,18 +168,17 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
   const int wc = m.k;   // EV_C wait count: the k rows of a token, one per down column tile
 
   // LDS carve-outs (task kinds never overlap in time inside one workgroup)
-  int* s_i = reinterpret_cast<int*>(smem);
-  uint32_t* rows_off = reinterpret_cast<uint32_t*>(smem);            // gemm: [16*MT]
-  int* fired = reinterpret_cast<int*>(smem + 512);                    // gemm2: fired tokens
-  void* tscratch = smem + 1024;                                       // gemm: tile LDS
+  int* s_i = reinterpret_cast<int*>(s0);                              // route / scan / group
+  uint32_t* rows_off = reinterpret_cast<uint32_t*>(gen + kGenRowsOff);  // gemm: [16*MT]
+  int* fired = reinterpret_cast<int*>(gen + kGenFired);                 // gemm2: fired tokens
 
-  auto meta = [&](int i) { return ld_rlx(&ra.hdr[HDR_META + i]); };
+  auto meta = [&](int i) ET_INLINE { return ld_rlx(&ra.hdr[HDR_META + i]); };
   // LDS copies of the per-expert row and block offsets (filled once per call
   // per workgroup, after the scan), so task decoding costs no memory trips
-  int* c_tok = reinterpret_cast<int*>(smem + sizeof(smem) - kIdxCache);
+  int* c_tok = reinterpret_cast<int*>(gen + kGenIdx);
   int* c_blk = c_tok + kMaxExperts + 1;
   bool cached = false;
-  auto load_cache = [&]() {
+  auto load_cache = [&]() ET_INLINE {
     if (cached) return;
     for (int e = tid; e <= m.E; e += kThreads) {
       c_tok[e] = ld_coh(&m.tok_indptr[e]);
@@ -186,7 +191,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
   // ordered column tile first, then block, so consecutive tasks share a
   // weight slice; e is the largest expert whose first task is <= t (experts
   // without rows own no tasks and share their successor's start)
-  auto decode = [&](int t, int nt, int& e, int& n, int& gb) {
+  auto decode = [&](int t, int nt, int& e, int& n, int& gb) ET_INLINE {
     int lo = 0, hi = m.E;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
   // columns and issues its k 16-byte row loads before summing, so a pass
   // costs two memory round trips.  The dynamic (inline) and tiled (static)
   // combines share this code and give bit-identical results.
-  auto combine = [&](int ntok, auto tok_of, int c0, int ncols, float* cw, int* cp) {
+  auto combine = [&](int ntok, auto tok_of, int c0, int ncols, float* cw, int* cp) ET_INLINE {
     const int k = m.k;
     for (int i = tid; i < ntok * k; i += kThreads) {
       const int t = tok_of(i / k), s = i % k;
@@ -245,60 +250,78 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
   // experts l, l + 64, ...; each of the k rounds takes the wave-wide largest
   // key, then the lowest expert index holding it (ties go to the lower index;
   // -0.0 and +0.0 share a key), with two DPP reductions and no LDS traffic.
-  auto route = [&](int r) {
+  auto route = [&](int r) ET_INLINE {
     int* hist_l = s_i;   // [E]
     for (int e = tid; e < m.E; e += kThreads) hist_l[e] = 0;
     __syncthreads();
     const int t0 = r * m.tpr;
     const int t1 = min(m.T, t0 + m.tpr);
-    const int nj = (m.E + 63) / 64;
-    for (int t = t0 + wave; t < t1; t += 4) {
-      const float* lg = m.logits + (size_t)t * m.E;
-      uint32_t keys[kMaxExperts / 64];
+    // NJ keys per lane (E <= 64 NJ); the logits of NB tokens of this wave
+    // (t0 + wave, t0 + wave + 4, ...) are requested before any is ranked
+    auto route_tokens = [&](auto nj_c, auto nb_c) ET_INLINE {
+      constexpr int NJ = decltype(nj_c)::value, NB = decltype(nb_c)::value;
+      for (int tb = t0 + wave; tb < t1; tb += 4 * NB) {
+        uint32_t kb[NB][NJ];
 #pragma unroll
-      for (int j = 0; j < kMaxExperts / 64; ++j) {
-        const int e = lane + 64 * j;
-        keys[j] = (j < nj && e < m.E) ? route_key32(lg[e]) : 0u;   // 0: below every key
-      }
-      uint32_t taken = 0;                  // bit j: my expert lane + 64 j already chosen
-      int my_e = -1;
-      uint32_t my_key = 0, key0 = 0;
-      for (int s = 0; s < m.k; ++s) {
-        uint32_t best = 0;
-        int best_e = 0x7fffffff;
+        for (int b = 0; b < NB; ++b) {
+          const int t = tb + 4 * b;
+          const float* lg = m.logits + (size_t)t * m.E;
 #pragma unroll
-        for (int j = 0; j < kMaxExperts / 64; ++j) {
-          const bool ok = j < nj && !((taken >> j) & 1u) && lane + 64 * j < m.E;
-          if (ok && keys[j] > best) {   // strict: equal keys keep the lower expert
-            best = keys[j];
-            best_e = lane + 64 * j;
+          for (int j = 0; j < NJ; ++j) {
+            const int e = lane + 64 * j;
+            kb[b][j] = (t < t1 && e < m.E) ? route_key32(lg[e]) : 0u;   // 0: below every key
           }
         }
-        const uint32_t top = wave_reduce_u32<true>(best);
-        const int e = (int)wave_reduce_u32<false>(best == top ? (uint32_t)best_e : 0xffffffffu);
-        if (s == 0) key0 = top;
-        if (lane == s) { my_e = e; my_key = top; }
-        if ((e & 63) == lane) taken |= 1u << (e >> 6);
-      }
-      // weights: softmax over the kept logits (= renormalised top-k softmax)
-      const float ex = lane < m.k ? expf(key_to_float(my_key) - key_to_float(key0)) : 0.f;
-      float sum = ex;
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) sum += __shfl_xor(sum, d);
-      if (lane < m.k) {
-        st_coh(&m.topk_ids[t * m.k + lane], my_e);
-        st_coh(&m.topk_w[t * m.k + lane], ex / sum);
-        atomicAdd(&hist_l[my_e], 1);
+        for (int b = 0; b < NB; ++b) {
+          const int t = tb + 4 * b;
+          if (t >= t1) break;
+          uint32_t taken = 0;                // bit j: my expert lane + 64 j already chosen
+          int my_e = -1;
+          uint32_t my_key = 0, key0 = 0;
+          for (int s = 0; s < m.k; ++s) {
+            uint32_t best = 0;
+            int best_e = 0x7fffffff;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+              const bool ok = !((taken >> j) & 1u) && lane + 64 * j < m.E;
+              if (ok && kb[b][j] > best) {   // strict: equal keys keep the lower expert
+                best = kb[b][j];
+                best_e = lane + 64 * j;
+              }
+            }
+            const uint32_t top = wave_reduce_u32<true>(best);
+            const int e = (int)wave_reduce_u32<false>(best == top ? (uint32_t)best_e : 0xffffffffu);
+            if (s == 0) key0 = top;
+            if (lane == s) { my_e = e; my_key = top; }
+            if ((e & 63) == lane) taken |= 1u << (e >> 6);
+          }
+          // weights: softmax over the kept logits (= renormalised top-k softmax)
+          const float ex = lane < m.k ? expf(key_to_float(my_key) - key_to_float(key0)) : 0.f;
+          float sum = ex;
+#pragma unroll
+          for (int d = 1; d < 64; d <<= 1) sum += __shfl_xor(sum, d);
+          if (lane < m.k) {
+            st_coh(&m.topk_ids[t * m.k + lane], my_e);
+            st_coh(&m.topk_w[t * m.k + lane], ex / sum);
+            atomicAdd(&hist_l[my_e], 1);
+          }
+        }
       }
-    }
+    };
+    using std::integral_constant;
+    if (m.E <= 64) route_tokens(integral_constant<int, 1>{}, integral_constant<int, 4>{});
+    else if (m.E <= 128) route_tokens(integral_constant<int, 2>{}, integral_constant<int, 4>{});
+    else if (m.E <= 256) route_tokens(integral_constant<int, 4>{}, integral_constant<int, 2>{});
+    else route_tokens(integral_constant<int, kMaxExperts / 64>{}, integral_constant<int, 1>{});
     __syncthreads();
     for (int e = tid; e < m.E; e += kThreads) st_coh(&m.hist[r * m.E + e], hist_l[e]);
   };
 
   // ------------------------------------------------------------- scan
-  auto scan = [&]() {
+  auto scan = [&]() ET_INLINE {
     int* hs = s_i;                         // [n_ne][E]
-    int* cnt = s_i + 16384;                // [E]
+    int* cnt = reinterpret_cast<int*>(s1); // [E]
     int* blk = cnt + 1024;                 // [E] -> block offsets
     int* tmp = blk + 1024;                 // [8]
     int* part = tmp + 8;                   // [256] chunk sums
@@ -369,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
   };
 
   // ------------------------------------------------------------- grouping
-  auto group = [&](int r) {
+  auto group = [&](int r) ET_INLINE {
     int* cur = s_i;            // [E] next position per expert
     int* base = s_i + 1024;    // [E] first position of this chunk per expert
     for (int e = tid; e < m.E; e += kThreads) {
@@ -380,26 +403,33 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
     __syncthreads();
     const int t0 = r * m.tpr;
     const int t1 = min(m.T, t0 + m.tpr);
-    if (wave == 0) {
-      for (int t = t0; t < t1; ++t) {      // tokens in order: stable positions
-        if (lane < m.k) {
-          const int e = ld_coh(&m.topk_ids[t * m.k + lane]);
-          const int pos = cur[e]++;        // a token's k experts are distinct
-          st_coh(&m.perm[pos], t * m.k + lane);
-          st_coh(&m.inv[t * m.k + lane], pos);
+    // the chunk's expert ids, loaded in parallel (chunks of up to 2048 pairs)
+    int* ids = s_i + 3072;
+    for (int q0 = t0 * m.k; q0 < t1 * m.k; q0 += 2048) {
+      const int q1 = min(t1 * m.k, q0 + 2048);
+      for (int q = q0 + tid; q < q1; q += kThreads) ids[q - q0] = ld_coh(&m.topk_ids[q]);
+      __syncthreads();
+      if (wave == 0) {
+        for (int q = q0; q < q1; q += m.k) {   // tokens in order: stable positions
+          if (lane < m.k) {
+            const int e = ids[q - q0 + lane];
+            const int pos = cur[e]++;        // a token's k experts are distinct
+            st_coh(&m.perm[pos], q + lane);
+            st_coh(&m.inv[q + lane], pos);
+          }
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
   };
 
   // ------------------------------------------------------------- gemm tiles
-  auto block_rows = [&](int gb, int e, int& pos0, int& pend) {
+  auto block_rows = [&](int gb, int e, int& pos0, int& pend) ET_INLINE {
     pos0 = c_tok[e] + (gb - c_blk[e]) * rows;
     pend = min(pos0 + rows, c_tok[e + 1]);
   };
 
-  auto gemm1 = [&](int t1g, int task) -> bool {
+  auto gemm1 = [&](int t1g, int task) ET_INLINE -> bool {
     load_cache();
     int e, n, gb, pos0, pend;
     decode(t1g, nt1, e, n, gb);
@@ -423,7 +453,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
       bo[Cfg::NH + j] = off;
     }
     const Rsrc rx = make_rsrc(m.x, (uint32_t)m.T * m.H * 2);
-    auto gate = [&](int round) -> bool {
+    auto gate = [&](int round) ET_INLINE -> bool {
       if (round != 0) return true;
       if ((sched == ET_SCHED_STATIC || sched == ET_SCHED_BARRIER) && !seen_group) {
         if (!wg_wait(c, EV_GROUP, NR, task)) return false;
@@ -439,10 +469,9 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
     Tile1 tile;
     bool ok;
     if constexpr (kWide)
-      ok = tile.run(rx, rows_off, rb, bo, (uint32_t)(m.H * 2), m.H, gate,
-                    static_cast<unsigned char*>(tscratch));
+      ok = tile.run(rx, rows_off, rb, bo, (uint32_t)(m.H * 2), m.H, gate, s0, s1, s2);
     else
-      ok = tile.run(rx, rows_off, rb, bo, m.H / kKBlock, gate, static_cast<float*>(tscratch));
+      ok = tile.run(rx, rows_off, rb, bo, m.H / kKBlock, gate, reinterpret_cast<float*>(s0));
     if (!ok) return false;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -473,7 +502,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
     return true;
   };
 
-  auto gemm2 = [&](int t2g, int task) -> bool {
+  auto gemm2 = [&](int t2g, int task) ET_INLINE -> bool {
     load_cache();
     int e, n2, gb, pos0, pend;
     decode(t2g, nt2, e, n2, gb);
@@ -489,7 +518,7 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
       bo[j] = (uint32_t)(n2 * bn2 + cw + 16 * j + lrow) * (uint32_t)(m.I * 2);
     }
     const Rsrc rh = make_rsrc(m.h, (uint32_t)m.T * m.k * m.I * 2);
-    auto gate = [&](int round) -> bool {
+    auto gate = [&](int round) ET_INLINE -> bool {
       if (round != 0) return true;
       if (sched == ET_SCHED_STATIC) {
         if (!wg_wait(c, m.ev_h + gb, nt1, task)) return false;
@@ -507,10 +536,9 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
     Tile2 tile;
     bool ok;
     if constexpr (kWide)
-      ok = tile.run(rh, rows_off, rb, bo, (uint32_t)(m.I * 2), m.I, gate,
-                    static_cast<unsigned char*>(tscratch));
+      ok = tile.run(rh, rows_off, rb, bo, (uint32_t)(m.I * 2), m.I, gate, s0, s1, s2);
     else
-      ok = tile.run(rh, rows_off, rb, bo, m.I / kKBlock, gate, static_cast<float*>(tscratch));
+      ok = tile.run(rh, rows_off, rb, bo, m.I / kKBlock, gate, reinterpret_cast<float*>(s0));
     if (!ok) return false;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -546,11 +574,11 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
     const int nf = sh.v[5];
     if (nf > 0)
       combine(nf, [&](int i) { return fired[i]; }, n2 * bn2, bn2,
-              reinterpret_cast<float*>(tscratch), reinterpret_cast<int*>(tscratch) + kMaxTopK * 128);
+              reinterpret_cast<float*>(s0), reinterpret_cast<int*>(s0) + kMaxTopK * 128);
     return true;
   };
 
-  auto combine_tile = [&](int t3, int task) -> bool {
+  auto combine_tile = [&](int t3, int task) ET_INLINE -> bool {
     if ((sched == ET_SCHED_STATIC || sched == ET_SCHED_BARRIER) && !seen_down) {
       if (!wg_wait(c, EV_DOWN, meta(MD_TOTAL2), task)) return false;
       seen_down = true;
@@ -561,12 +589,12 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
     const int ntok = min(m.T, t0 + kCombTok) - t0;
     const int c0 = cc * kCombCols;
     combine(ntok, [&](int i) { return t0 + i; }, c0, min(kCombCols, m.H - c0),
-            reinterpret_cast<float*>(tscratch), reinterpret_cast<int*>(tscratch) + kMaxTopK * 128);
+            reinterpret_cast<float*>(s0), reinterpret_cast<int*>(s0) + kMaxTopK * 128);
     return true;
   };
 
   // ------------------------------------------------------------- dispatch
-  auto run = [&](int task) -> bool {
+  auto run = [&](int task) ET_INLINE -> bool {
     if (task < NR) {
       route(task);
       if (sched == ET_SCHED_PER_OP) return true;

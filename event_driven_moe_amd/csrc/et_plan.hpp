@@ -7,6 +7,9 @@
 #include <hip/hip_runtime.h>
 
 #define ET_HD __host__ __device__ __forceinline__
+// lambdas inside the persistent kernels: inlined even when called from
+// several places (an outlined task body costs a call frame in scratch)
+#define ET_INLINE __attribute__((always_inline))
 
 namespace et {
 
@@ -118,7 +121,7 @@ constexpr int kCombTok = 16;
 constexpr int kCombCols = 256;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
-constexpr int kHistEntries = 16384;   // n_route * E must fit (int32, in LDS)
+constexpr int kHistEntries = 8192;    // n_route * E must fit (int32, 32 KB of LDS)
 
 enum : int { EV_ROUTE = 0, EV_SCAN = 1, EV_GROUP = 2, EV_G1ALL = 3, EV_DOWN = 4, EV_FIXED = 8 };
 

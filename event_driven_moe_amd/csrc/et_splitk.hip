@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kThreads, 1) void splitk_kernel(RunArgs ra, SplitKA
   const int ev_all = s.n_max;
   const int sched = ra.sched;
 
-  auto run = [&](int task) -> bool {
+  auto run = [&](int task) ET_INLINE -> bool {
     if (task < n1) {
       const int i = task >> 2, j = task & 3;
       splitk_stage1(s, i, j);

@@ -73,10 +73,11 @@ def test_modes_bit_identical(name, T):
         assert np.array_equal(o, outs[0])
 
 
-def moe_tiling(T, tile=-1):
+def moe_tiling(T, k, tile=-1):
     """(rows per block, h columns per gate/up task, columns per down task) of
-    the library's tile variant for T tokens (or the forced variant)."""
-    tv = tile if tile >= 0 else (0 if T <= 16 else 1 if T <= 32 else 2 if T <= 128 else
+    the library's tile variant for T tokens routed to k experts each (or the
+    forced variant)."""
+    tv = tile if tile >= 0 else (0 if T <= 16 else 1 if T <= 32 else 2 if T * k <= 256 else
                                  3 if T <= 512 else 4)
     return {0: (16, 16, 16), 1: (32, 16, 16), 2: (64, 16, 16), 3: (64, 128, 256),
             4: (128, 128, 256)}[tv]
@@ -107,8 +108,8 @@ def test_event_invariants(sched):
     cfg, _, _, _, out, aux, _ = run_moe(name, T, sched, ws=ws, debug=et.DEBUG_COUNTS)
     st = ws.status()
     E, k, H, I = cfg["n_experts"], cfg["top_k"], cfg["hidden"], cfg["inter"]
-    nr = min(128, 16384 // E)
-    rows, bn1, bn2 = moe_tiling(T)
+    nr = min(128, 8192 // E)
+    rows, bn1, bn2 = moe_tiling(T, k)
     tab = oev.moe_table(aux["counts"], rows, I, bn1, H, bn2, nr)
     ncomb = -(-T // 16) * -(-H // 256) if sched == "static" else 0
     total = sum(tab["tasks"].values()) + ncomb
