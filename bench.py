@@ -91,14 +91,99 @@ def cpu_baseline(cfg, logits, x, wg, wu, wd, T, target_s=15.0):
     t0 = time.perf_counter()
     omoe.moe_layer(L, X, cfg["top_k"], weights, tokens=rng.choice(T, n, replace=False))
     dt = time.perf_counter() - t0
+    # a token sample sized for about target_s of oracle work, repeated
+    # until that much time has passed
     n2 = int(min(T, max(n, n * target_s / max(dt, 1e-3))))
     sample = np.sort(rng.choice(T, n2, replace=False))
+    reps = 0
     t0 = time.perf_counter()
-    omoe.moe_layer(L, X, cfg["top_k"], weights, tokens=sample)
+    while reps == 0 or time.perf_counter() - t0 < target_s:
+        omoe.moe_layer(L, X, cfg["top_k"], weights, tokens=sample)
+        reps += 1
     dt = time.perf_counter() - t0
-    return {"value": n2 / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": "%d of %d tokens (routing and grouping of all %d), fp64 numpy, %.1f s"
-                      % (n2, T, T, dt)}
+    return {"value": reps * n2 / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d pass(es) over %d of %d tokens (each pass routes and groups all %d), "
+                      "fp64 numpy, %.1f s" % (reps, n2, T, T, dt)}
+
+
+COPY_BYTES = 1 << 30   # calibration copy: reads and writes 1 GiB
+
+
+def copy_calibration():
+    """A plain device copy of known size, so that one profiled run holds both
+    the MoE kernel and a reference for the HBM byte counters."""
+    import torch
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
+def _pmc_per_dispatch(db, counter):
+    """{kernel name: [per-dispatch value]} of one counter in a rocprofv3 DB."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    out = {}
+    for _, kn, v in con.execute(
+            "select dispatch_id, kernel_name, sum(value) from counters_collection "
+            "where counter_name = ? group by dispatch_id order by dispatch_id", (counter,)):
+        out.setdefault(kn, []).append(v)
+    return out
+
+
+def kernel_stats(db):
+    """Per-kernel launch statistics of a rocprofv3 --kernel-trace database, in
+    the form the profiles keep (the stats CSV is not always written when the
+    profiled process exits)."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = {}
+    for name, dur, vgpr, agpr, lds, scr in con.execute(
+            "select name, duration, vgpr_count, accum_vgpr_count, lds_size, scratch_size from kernels"):
+        r = rows.setdefault(name, {"d": [], "res": (vgpr, agpr, lds, scr)})
+        r["d"].append(dur / 1000.0)
+    total = sum(sum(r["d"]) for r in rows.values())
+    print("| kernel | calls | total us | avg us | median us | min us | max us | % | VGPR/AGPR/LDS B/scratch B |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for name, r in sorted(rows.items(), key=lambda kv: -sum(kv[1]["d"])):
+        d = sorted(r["d"])
+        short = name if len(name) < 60 else name[:57] + "..."
+        print("| %s | %d | %.1f | %.2f | %.2f | %.2f | %.2f | %.1f | %s |" % (
+            short, len(d), sum(d), sum(d) / len(d), d[len(d) // 2], d[0], d[-1],
+            100.0 * sum(d) / total, "/".join(str(x) for x in r["res"])))
+
+
+def traffic_summary(fetch_db, write_db, key):
+    """HBM bytes per launch of the MoE kernel from a FETCH_SIZE run and a
+    WRITE_SIZE run (both KiB per dispatch), each scaled by what the counter
+    reads for the calibration copy; stores the figure for later bench lines."""
+    res = {}
+    for name, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
+        d = _pmc_per_dispatch(db, name)
+        moe = [v for k, vs in d.items() if "moe_kernel" in k for v in vs]
+        cpy = [v for k, vs in d.items() if "moe_kernel" not in k for v in vs
+               if abs(v * 1024 - COPY_BYTES) < 0.6 * COPY_BYTES]
+        if not moe or not cpy:
+            raise SystemExit("%s: no MoE kernel or calibration copy dispatches in %s" % (name, db))
+        cal = COPY_BYTES / (1024.0 * sum(cpy) / len(cpy))
+        res[name] = {"kib_per_dispatch": sum(moe) / len(moe), "dispatches": len(moe),
+                     "copy_kib": sum(cpy) / len(cpy), "scale": cal,
+                     "bytes": 1024.0 * cal * sum(moe) / len(moe)}
+    ent = {"kernel_hash": kernel_source_hash(),
+           "hbm_bytes_per_launch": int(res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"]),
+           "read_bytes": int(res["FETCH_SIZE"]["bytes"]), "write_bytes": int(res["WRITE_SIZE"]["bytes"]),
+           "counters": res}
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            tj = json.load(fh)
+    except (OSError, ValueError):
+        tj = {}
+    tj[key] = ent
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(tj, fh, indent=1, sort_keys=True)
+    print(json.dumps({key: ent}, indent=1))
 
 
 def main():
@@ -112,7 +197,21 @@ def main():
     ap.add_argument("--fetch", type=int, default=4)
     ap.add_argument("--modes", action="store_true", help="also time the other schedules")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB device copy before timing (reference for HBM counters)")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="no GPU work: read two rocprofv3 --pmc databases (FETCH_SIZE, "
+                         "WRITE_SIZE) of this command and record the MoE kernel's HBM bytes")
+    ap.add_argument("--kernel-stats", metavar="DB",
+                    help="no GPU work: print per-kernel statistics of a rocprofv3 --kernel-trace database")
     args = ap.parse_args()
+    if args.kernel_stats:
+        kernel_stats(args.kernel_stats)
+        return
+    if args.traffic:
+        traffic_summary(args.traffic[0], args.traffic[1],
+                        "%s:T%d:%s" % (args.workload, args.tokens, args.sched))
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -143,6 +242,8 @@ def main():
     max_rows = int(aux["counts"].max().item())
     alg = algorithmic(cfg, T, n_active)
 
+    if args.copy_calibration:
+        copy_calibration()
     torch.cuda.synchronize()
     per, wall = time_calls(step, args.steps, args.warmup)
     torch.cuda.synchronize()

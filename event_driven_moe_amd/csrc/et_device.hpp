@@ -300,14 +300,16 @@ __device__ __forceinline__ int wg_pop(const Ctx& c, PopState& ps) {
   int t = -1;
   if (threadIdx.x == 0) {
     if (ps.left == 0) {
-      // `fetch` slots per atomic only when that many are already published
-      // (pushed or initial) beyond the claim counter: a worker never holds
-      // published tasks while it waits for an unpublished one, and short
-      // leading phases spread over all workers.  A racy peek is enough: any
-      // claim size is correct.
+      // Claim size: up to `fetch` slots per atomic, but no more than this
+      // worker's share of the published (pushed or initial) slots beyond the
+      // claim counter.  A worker then never holds published tasks while
+      // others idle or while it waits for an unpublished slot, and a short
+      // phase of long tasks spreads over all workers.  A racy peek is
+      // enough: any claim size is correct.
       const int head = ld_rlx(&c.a.hdr[HDR_QHEAD]);
       const int avail = c.a.n_init + ld_rlx(&c.a.hdr[HDR_QPUSH]) - head;
-      const int sz = (head < c.a.n_single || avail < c.a.fetch) ? 1 : c.a.fetch;
+      int sz = avail / c.G;
+      sz = head < c.a.n_single ? 1 : (sz < 1 ? 1 : (sz > c.a.fetch ? c.a.fetch : sz));
       ps.base = add_rlx(&c.a.hdr[HDR_QHEAD], sz);
       ps.size = sz;
       ps.left = sz;
