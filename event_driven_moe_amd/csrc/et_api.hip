@@ -82,6 +82,8 @@ int fill_common(LaunchCommon& lc, void* ws, const et_plan* plan, int sched, cons
   lc.timeout_ms = o && o->timeout_ms > 0 ? o->timeout_ms : 2000;
   lc.tile = o ? o->tile : -1;
   if (o && (o->tile < -1 || o->tile >= TV_COUNT)) return ET_EINVAL;
+  lc.coop = o ? o->launch : ET_LAUNCH_ORDINARY;
+  if (lc.coop != ET_LAUNCH_ORDINARY && lc.coop != ET_LAUNCH_COOPERATIVE) return ET_EINVAL;
   lc.stream = stream;
   return workers_for_current_device(&lc.G);
 }

@@ -18,18 +18,21 @@ struct LaunchCommon {
   int debug;
   int timeout_ms;
   int tile;
+  int coop;            // persistent launches: cooperative (1) or ordinary (0)
   int G;               // workgroups of a persistent launch (one per CU)
   hipStream_t stream;
 
   RunArgs run_args() const;
 
-  // Launches kernel(ra, args).  Persistent launches are cooperative: every
-  // workgroup must be resident, since tasks spin on each other's events.
+  // Launches kernel(ra, args).  `persistent`: every workgroup must be
+  // resident, since tasks spin on each other's events -- cooperative when the
+  // caller asked for the guarantee, else an ordinary launch of one workgroup
+  // per compute unit (one fits per unit).
   template <class A>
-  int launch(const void* kernel, RunArgs* ra, A* args, bool cooperative) const {
+  int launch(const void* kernel, RunArgs* ra, A* args, bool persistent) const {
     void* kargs[] = {ra, args};
     hipError_t e;
-    if (cooperative)
+    if (persistent && coop)
       e = hipLaunchCooperativeKernel(kernel, dim3(G), dim3(kThreads), kargs, 0, stream);
     else
       e = hipLaunchKernel(kernel, dim3(G), dim3(kThreads), kargs, 0, stream);

@@ -20,6 +20,12 @@
 //                    EV_H[gb] only, not on all gate/up tasks -- the event that
 //                    removes the barrier between the two GroupGEMMs;
 //   combine          out[t] = sum_s w[t, s] y[inv[t, s]] in slot order.
+// Static and dynamic modes run the scan inline in the routing task whose
+// notify completes EV_ROUTE (the notify that fires an event runs its single
+// consumer, with no queue slot or wait), and when few pairs were routed
+// (T * k <= kInlinePairs) the same workgroup also groups all chunks right
+// after the scan.  The barrier and per-operator baselines keep them as tasks
+// of their own.
 // Dynamic mode: the notify that zeroes EV_EXP[e] pushes expert e's task range
 // tasks[task_indptr[e] : task_indptr[e+1]] (data-dependent fan-out), the one
 // that zeroes EV_H[gb] pushes block gb's down tasks, and the one that zeroes
@@ -165,6 +171,9 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
   const int nt1 = m.I / bn1, nt2 = m.H / bn2;
   const int NR = m.NR;
   const int base1 = 2 * NR + 1;
+  // static / dynamic with few routed pairs: grouping runs inline after the scan
+  const bool inline_group = (sched == ET_SCHED_STATIC || sched == ET_SCHED_DYNAMIC) &&
+                            m.T * m.k <= kInlinePairs;
   const int wc = m.k;   // EV_C wait count: the k rows of a token, one per down column tile
 
   // LDS carve-outs (task kinds never overlap in time inside one workgroup)
@@ -423,6 +432,34 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
     }
   };
 
+  // Grouping of every chunk by the workgroup that just ran the scan: the
+  // scan left the per-(chunk, expert) offsets in LDS (hs, relative to the
+  // expert's first row tokp[e]); wave w takes chunks w, w + 4, ... and uses
+  // those offsets as its cursors.  The routed ids are staged in LDS first.
+  auto group_inline = [&]() ET_INLINE {
+    int* hs = s_i;
+    const int* tokp = reinterpret_cast<const int*>(s1);
+    int* ids = reinterpret_cast<int*>(gen + kGenIdx);   // [T * k] (the index cache is not yet in use)
+    cached = false;
+    const int np = m.T * m.k;
+    for (int q = tid; q < np; q += kThreads) ids[q] = ld_coh(&m.topk_ids[q]);
+    __syncthreads();
+    const int n_ne = cdiv(m.T, m.tpr);
+    for (int r = wave; r < n_ne; r += 4) {
+      const int t1 = min(m.T, (r + 1) * m.tpr);
+      for (int t = r * m.tpr; t < t1; ++t) {   // tokens in order: stable positions
+        if (lane < m.k) {
+          const int q = t * m.k + lane;
+          const int e = ids[q];
+          const int pos = tokp[e] + hs[r * m.E + e]++;   // a token's k experts are distinct
+          st_coh(&m.perm[pos], q);
+          st_coh(&m.inv[q], pos);
+        }
+      }
+    }
+    __syncthreads();
+  };
+
   // ------------------------------------------------------------- gemm tiles
   auto block_rows = [&](int gb, int e, int& pos0, int& pend) ET_INLINE {
     pos0 = c_tok[e] + (gb - c_blk[e]) * rows;
@@ -599,26 +636,60 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
       route(task);
       if (sched == ET_SCHED_PER_OP) return true;
       wg_release();
-      if (sched != ET_SCHED_DYNAMIC) {
+      if (sched == ET_SCHED_BARRIER) {
         t0_notify(c, EV_ROUTE, 1, NR, task);
-      } else if (wg_notify(c, EV_ROUTE, 1, NR, task)) {
-        wg_push(c, 1, [&](int) { return NR; });          // the scan task
+        return true;
       }
+      if (!wg_notify(c, EV_ROUTE, 1, NR, task)) return true;
+      // this notify completed EV_ROUTE: the scan runs here
+      long long ts = trace_now(c);
+      const int nb = scan();
+      count_run(c, NR);
+      trace_task(c, NR, ts);
+      if (!inline_group) {
+        if (sched == ET_SCHED_DYNAMIC) {
+          set_total(c, 2 * NR + nb * (nt1 + nt2));
+          wg_release();
+          wg_push(c, NR, [&](int i) { return NR + 1 + i; });   // the grouping tasks
+        } else {
+          wg_release();
+          t0_notify(c, EV_SCAN, 1, 1, NR);
+        }
+        return true;
+      }
+      ts = trace_now(c);
+      group_inline();
+      for (int r = 0; r < NR; ++r) {
+        count_run(c, NR + 1 + r);
+        trace_task(c, NR + 1 + r, ts);
+      }
+      wg_release();
+      if (sched == ET_SCHED_STATIC) {
+        t0_notify(c, EV_SCAN, 1, 1, NR);
+        t0_notify(c, EV_GROUP, NR, NR, NR + 1);
+        return true;
+      }
+      // dynamic: every expert event receives all of its rows at once (its
+      // data-dependent wait count) and fires; the fired experts' task ranges
+      // together are the whole gate/up range, pushed in one piece
+      set_total(c, NR + nb * (nt1 + nt2));
+      for (int e = tid; e < m.E; e += kThreads) {
+        const int n = ld_coh(&m.counts[e]);
+        if (n > 0) {
+          const int old = add_rlx(c.ev + m.ev_exp + e, -n);
+          if (old != 0) raise_fault(ra, ET_ESTATE, NR + 1, m.ev_exp + e, old - n);
+        }
+      }
+      const int total1 = nb * nt1;
+      wg_push(c, total1, [&](int i) { return base1 + i; });
       return true;
     }
-    if (task == NR) {
-      if (sched != ET_SCHED_PER_OP && sched != ET_SCHED_DYNAMIC)
-        if (!wg_wait(c, EV_ROUTE, NR, task)) return false;
-      const int nb = scan();
+    if (task == NR) {   // the scan as a task of its own: barrier and per-op modes
+      if (sched == ET_SCHED_BARRIER && !wg_wait(c, EV_ROUTE, NR, task)) return false;
+      scan();
       if (sched == ET_SCHED_PER_OP) return true;
-      if (sched == ET_SCHED_DYNAMIC) {
-        set_total(c, base1 + nb * (nt1 + nt2));
-        wg_release();
-        wg_push(c, NR, [&](int i) { return NR + 1 + i; });   // the grouping tasks
-      } else {
-        wg_release();
-        t0_notify(c, EV_SCAN, 1, 1, task);
-      }
+      wg_release();
+      t0_notify(c, EV_SCAN, 1, 1, task);
       return true;
     }
     if (task < base1) {
@@ -700,13 +771,13 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
       if (ok) count_run(c, t);
       if (ok) trace_task(c, t, t0);
     }
-    if (ok && c.wg == c.G - 1) {
+    if (ok && sched == ET_SCHED_BARRIER && c.wg == c.G - 1) {
       const long long t0 = trace_now(c);
       ok = run(NR);
       if (ok) count_run(c, NR);
       if (ok) trace_task(c, NR, t0);
     }
-    for (int r = c.wg; ok && r < NR; r += c.G) {
+    for (int r = c.wg; ok && !inline_group && r < NR; r += c.G) {
       const long long t0 = trace_now(c);
       ok = run(NR + 1 + r);
       if (ok) count_run(c, NR + 1 + r);
@@ -760,14 +831,14 @@ int launch_moe(const LaunchCommon& lc, const float* logits, const uint16_t* x, i
   m.I = p->inter;
   m.E = p->n_experts;
   m.k = p->top_k;
-  m.NR = mp.n_route;
+  m.NR = mp.routes(T);
   m.tpr = mp.tpr(T);
   m.ev_exp = mp.ev_exp();
   m.ev_h = mp.ev_h();
   m.ev_c = mp.ev_c();
   RunArgs ra = lc.run_args();
-  ra.n_init = mp.n_route;
-  ra.n_single = 2 * mp.n_route + 1;   // routing, scan and grouping: one slot per claim
+  ra.n_init = m.NR;
+  ra.n_single = 2 * m.NR + 1;   // routing and grouping: one slot per claim
   ra.total_hint = kUnknownTotal;
   ra.extent = mp.extent(T, tl);
   const void* const kernels[TV_COUNT] = {

@@ -102,8 +102,8 @@ struct MlpPlan {
 
 // ---------------------------------------------------------------------------
 // MoE layer.
-// Routing / grouping use n_route token chunks; chunk r covers tokens
-// [r * tpr, min((r + 1) * tpr, T)) with tpr = ceil(T / n_route).
+// Routing / grouping use R = routes(T) <= n_route token chunks; chunk r
+// covers tokens [r * tpr, min((r + 1) * tpr, T)) with tpr = ceil(T / R).
 // events (prefix of a bank):
 //   EV_ROUTE  all routing tasks done      (wait count n_route)
 //   EV_SCAN   scan done                   (1)
@@ -122,6 +122,8 @@ constexpr int kCombCols = 256;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kHistEntries = 8192;    // n_route * E must fit (int32, 32 KB of LDS)
+constexpr int kRouteTok = 8;          // tokens per routing chunk (fewer chunks when T is small)
+constexpr int kInlinePairs = 2048;    // T * k up to this: grouping runs inline after the scan
 
 enum : int { EV_ROUTE = 0, EV_SCAN = 1, EV_GROUP = 2, EV_G1ALL = 3, EV_DOWN = 4, EV_FIXED = 8 };
 
@@ -140,7 +142,12 @@ struct MoePlan {
   ET_HD int max_tasks() const {
     return 2 * n_route + 1 + nb_max() * (inter / kMinCols + hidden / kMinCols) + n_comb(t_max);
   }
-  ET_HD int tpr(int T) const { return cdiv(T, n_route); }
+  // routing chunks of a call: about kRouteTok tokens each, at most n_route
+  ET_HD int routes(int T) const {
+    const int r = cdiv(T, kRouteTok);
+    return r < 1 ? 1 : (r > n_route ? n_route : r);
+  }
+  ET_HD int tpr(int T) const { return cdiv(T, routes(T)); }
 };
 
 ET_HD int moe_n_route(int n_experts) {

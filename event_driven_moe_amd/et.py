@@ -27,7 +27,7 @@ c_int, c_size_t, c_void_p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 
 class Opts(ctypes.Structure):
     _fields_ = [("fetch_batch", c_int), ("debug_flags", c_int), ("timeout_ms", c_int),
-                ("tile", c_int)]
+                ("tile", c_int), ("launch", c_int)]
 
 
 class Plan(ctypes.Structure):
@@ -131,8 +131,12 @@ def _ptr(t, dtype, name, shape=None):
     return c_void_p(t.data_ptr())
 
 
-def _opts(fetch_batch=4, debug=0, timeout_ms=2000, tile=-1):
-    return Opts(fetch_batch, debug, timeout_ms, tile)
+LAUNCH_ORDINARY, LAUNCH_COOPERATIVE = 0, 1
+
+
+def _opts(fetch_batch=4, debug=0, timeout_ms=2000, tile=-1, cooperative=False):
+    return Opts(fetch_batch, debug, timeout_ms, tile,
+                LAUNCH_COOPERATIVE if cooperative else LAUNCH_ORDINARY)
 
 
 def plan_workspace(workload, max_tokens, hidden=0, inter=0, n_experts=0, top_k=0):

@@ -77,12 +77,27 @@ enum {
   ET_DEBUG_TRACE = 2    /* record each task's workgroup and start / end time (et_layout.trace) */
 };
 
+/* Launch modes of the persistent kernels.  Every workgroup of a persistent
+ * launch must be resident at the same time, since tasks wait on each other.
+ * The kernels launch one workgroup per compute unit and are sized so that one
+ * fits per unit, so an ordinary launch makes them all resident whenever no
+ * other kernel holds compute units indefinitely.  A cooperative launch
+ * guarantees co-residency even on a shared device, but the runtime separates
+ * it from the previous kernel by a device-wide drain (about 20 us on MI355X).
+ * Under either mode a workgroup that never becomes resident makes the others'
+ * waits end in ET_ETIMEOUT, not a hang. */
+enum {
+  ET_LAUNCH_ORDINARY = 0,     /* default */
+  ET_LAUNCH_COOPERATIVE = 1
+};
+
 /* Per-call options; pass NULL for the defaults. */
 typedef struct et_opts {
   int fetch_batch;   /* dynamic mode: queue slots claimed per atomic (1..8; default 4) */
   int debug_flags;   /* ET_DEBUG_* (default 0) */
   int timeout_ms;    /* watchdog for every wait / queue spin (default 2000 ms) */
   int tile;          /* MoE / MLP tile-variant override (-1 = chosen from the token count) */
+  int launch;        /* ET_LAUNCH_* (default ET_LAUNCH_ORDINARY) */
 } et_opts;
 
 /* Workspace plan: dimensions and byte offsets of every region.  Filled by

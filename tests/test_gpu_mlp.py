@@ -107,3 +107,14 @@ def test_invariants(ws, weights):
         cnt = ws.counters(1 - st["bank"]).cpu().numpy()
         nht = I // 128
         assert (cnt[:mb * nht] == -8).all() and (cnt[mb * nht:-1] == 0).all()
+
+
+@pytest.mark.parametrize("sched", ["static", "dynamic"])
+def test_cooperative_launch(ws, weights, sched):
+    """The cooperative launch mode runs the same kernel: same results."""
+    wg, wu, wd, wgT, wuT, wdT = weights
+    x = synth.mlp_inputs(16, H, I, device=DEV)[0]
+    y0 = _run(ws, x, wgT, wuT, wdT, sched)
+    y1 = _run(ws, x, wgT, wuT, wdT, sched, cooperative=True)
+    assert np.array_equal(y0, y1)
+    assert_rel(y1, om.mlp(to_np(x), to_np(wg), to_np(wu), to_np(wd)), 1e-2, "y")

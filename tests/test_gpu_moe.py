@@ -97,18 +97,19 @@ def test_fetch_batches(fetch):
     check_against_oracle("moe_skewed", 256, out, aux)
 
 
+@pytest.mark.parametrize("T", [256, 1024])
 @pytest.mark.parametrize("sched", ["static", "dynamic"])
-def test_event_invariants(sched):
+def test_event_invariants(sched, T):
     """Each task ran once; the data-dependent expert events ended at their
     run-time wait counts (rows routed to each expert), block events at the
     number of gate/up tiles of a block."""
-    name, T = "moe_skewed", 256
+    name = "moe_skewed"
     ws = _ws(name, 1024)
     ws.runs().zero_()
     cfg, _, _, _, out, aux, _ = run_moe(name, T, sched, ws=ws, debug=et.DEBUG_COUNTS)
     st = ws.status()
     E, k, H, I = cfg["n_experts"], cfg["top_k"], cfg["hidden"], cfg["inter"]
-    nr = min(128, 8192 // E)
+    nr = min(128, 8192 // E, -(-T // 8))   # routing chunks of about 8 tokens
     rows, bn1, bn2 = moe_tiling(T, k)
     tab = oev.moe_table(aux["counts"], rows, I, bn1, H, bn2, nr)
     ncomb = -(-T // 16) * -(-H // 256) if sched == "static" else 0
@@ -189,3 +190,12 @@ def test_symbolic_token_counts_one_workspace():
         for sched in ("dynamic", "static"):
             _, _, _, _, out, aux, _ = run_moe("moe_skewed", T, sched, ws=ws)
             check_against_oracle("moe_skewed", T, out, aux)
+
+
+@pytest.mark.parametrize("sched", ["static", "dynamic"])
+def test_cooperative_launch(sched):
+    """The cooperative launch mode runs the same kernel: same results."""
+    _, _, _, _, out0, aux0, _ = run_moe("moe_skewed", 256, sched)
+    _, _, _, _, out1, aux1, _ = run_moe("moe_skewed", 256, sched, cooperative=True)
+    assert np.array_equal(out0, out1)
+    check_against_oracle("moe_skewed", 256, out1, aux1)

@@ -98,3 +98,14 @@ def test_bad_rows_rejected(ws):
     with pytest.raises(et.EtError) as e:
         et.splitk_reduce(A, torch.zeros((4096, 4), device=DEV), torch.zeros(4096, device=DEV), ws)
     assert e.value.code == et.EWORKSPACE
+
+
+@pytest.mark.parametrize("sched", ["static", "dynamic"])
+def test_cooperative_launch(ws, sched):
+    """The cooperative launch mode runs the same kernel: same results."""
+    A = synth.splitk_inputs(rows=2048, seed=12, device=DEV)
+    B0, C0 = _run(ws, A, sched)
+    B1, C1 = _run(ws, A, sched, cooperative=True)
+    assert np.array_equal(B0, B1) and np.array_equal(C0, C1)
+    _, Cref = osk.splitk_reduce(A.cpu().numpy())
+    assert_rel(C1, Cref, 1e-5, "C")
