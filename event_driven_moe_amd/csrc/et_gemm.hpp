@@ -180,11 +180,13 @@ struct RingTile {
   // s0, s1, s2: the three ring slots, three distinct __shared__ arrays of
   // kStageBytes each -- distinct objects let the compiler wait only for the
   // copies into the slot being read, so two stages stay in flight.
+  // mv: 16-row groups holding valid rows (1..MT); the MFMAs of the others
+  // are skipped (their rows read as zeros and their results are not stored).
   template <class Gate>
   __device__ __forceinline__ bool run(Rsrc ra, const uint32_t* a_row_off /* [kRows], LDS */,
                                       const Rsrc* rb, const uint32_t* b_row0, uint32_t b_stride,
                                       int K, Gate gate, unsigned char* s0, unsigned char* s1,
-                                      unsigned char* s2) {
+                                      unsigned char* s2, int mv = MT) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nks = K / 64;
@@ -251,6 +253,9 @@ struct RingTile {
         issue_a(ks + 2, nxt2);
       }
       const unsigned char* sb = cur + kRows * 128 + wave * 64 * 128;
+      // each 32-element K-step reads all of its fragments first, then runs
+      // its MFMAs (the LDS latency is paid once per K-step); 32-row halves
+      // beyond the valid rows are skipped
 #pragma unroll
       for (int s2i = 0; s2i < 2; ++s2i) {
         i32x4 bf[4], af[MT];
@@ -258,12 +263,22 @@ struct RingTile {
         for (int n = 0; n < 4; ++n)
           bf[n] = *reinterpret_cast<const i32x4*>(sb + n * 16 * 128 + foff[s2i]);
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-          af[m] = *reinterpret_cast<const i32x4*>(cur + m * 16 * 128 + foff[s2i]);
+        for (int m = 0; m < MT; m += 2)
+          if (m < mv) {
+            af[m] = *reinterpret_cast<const i32x4*>(cur + m * 16 * 128 + foff[s2i]);
+            af[m + 1] = *reinterpret_cast<const i32x4*>(cur + (m + 1) * 16 * 128 + foff[s2i]);
+          }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+        for (int m = 0; m < MT; m += 2)
+          if (m < mv) {
 #pragma unroll
-          for (int n = 0; n < 4; ++n) acc[m][n] = mfma16(af[m], bf[n], acc[m][n]);
+            for (int n = 0; n < 4; ++n) {
+              acc[m][n] = mfma16(af[m], bf[n], acc[m][n]);
+              acc[m + 1][n] = mfma16(af[m + 1], bf[n], acc[m + 1][n]);
+            }
+          }
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     for (int ks = 0; ks < nks; ks += 3) {

@@ -29,9 +29,10 @@ struct MlpArgs {
 };
 
 template <int MT> constexpr int kMlpPD = MT == 1 ? 4 : (MT == 2 ? 3 : 2);   // K-blocks in flight
+template <int MT> constexpr int kMlpOcc = 1;                               // workgroups per CU
 
 template <int MT>
-__global__ __launch_bounds__(kThreads, 1) void mlp_kernel(RunArgs ra, MlpArgs m) {
+__global__ __launch_bounds__(kThreads, kMlpOcc<MT>) void mlp_kernel(RunArgs ra, MlpArgs m) {
   __shared__ Shared sh;
   __shared__ uint32_t rows_off[16 * MT];
   using Tile1 = StreamTile<MT, 2, 4, kMlpPD<MT>, false>;   // reads x
@@ -183,15 +184,17 @@ int launch_mlp(const LaunchCommon& lc, const uint16_t* x, int B, const uint16_t*
   const void* k = tv == TV_M16   ? reinterpret_cast<const void*>(&mlp_kernel<1>)
                   : tv == TV_M32 ? reinterpret_cast<const void*>(&mlp_kernel<2>)
                                  : reinterpret_cast<const void*>(&mlp_kernel<4>);
+  LaunchCommon l = lc;
+  l.G = lc.G * (tv == TV_M16 ? kMlpOcc<1> : tv == TV_M32 ? kMlpOcc<2> : kMlpOcc<4>);
   if (lc.sched == ET_SCHED_PER_OP) {
     for (int ph = 0; ph < 2; ++ph) {
       ra.phase = ph;
-      int e = lc.launch(k, &ra, &m, false);
+      int e = l.launch(k, &ra, &m, false);
       if (e) return e;
     }
     return ET_OK;
   }
-  return lc.launch(k, &ra, &m, true);
+  return l.launch(k, &ra, &m, true);
 }
 
 }  // namespace et

@@ -129,6 +129,7 @@ struct MoeCfg {
   static constexpr int NH = kWide ? 2 : 1;          // 16-column h groups per wave (gate/up)
   static constexpr int NB2 = kWide ? 4 : 1;         // 16-column groups per wave (down)
   static constexpr int PD = MT == 1 ? 4 : (MT == 2 ? 3 : 2);
+  static constexpr int kOcc = 1;                    // workgroups per CU
 };
 
 template <int TV, bool COH, int NB>
@@ -149,7 +150,7 @@ __device__ __forceinline__ int xcd_pos(int w, int G) {
 }
 
 template <int TV>
-__global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m) {
+__global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs ra, MoeArgs m) {
   using Cfg = MoeCfg<TV>;
   using Tile1 = typename TileOf<TV, false, 2 * Cfg::NH>::type;   // gate/up: reads x
   using Tile2 = typename TileOf<TV, true, Cfg::NB2>::type;       // down: reads h (this launch)
@@ -506,7 +507,8 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
     Tile1 tile;
     bool ok;
     if constexpr (kWide)
-      ok = tile.run(rx, rows_off, rb, bo, (uint32_t)(m.H * 2), m.H, gate, s0, s1, s2);
+      ok = tile.run(rx, rows_off, rb, bo, (uint32_t)(m.H * 2), m.H, gate, s0, s1, s2,
+                    cdiv(pend - pos0, 16));
     else
       ok = tile.run(rx, rows_off, rb, bo, m.H / kKBlock, gate, reinterpret_cast<float*>(s0));
     if (!ok) return false;
@@ -573,7 +575,8 @@ __global__ __launch_bounds__(kThreads, 1) void moe_kernel(RunArgs ra, MoeArgs m)
     Tile2 tile;
     bool ok;
     if constexpr (kWide)
-      ok = tile.run(rh, rows_off, rb, bo, (uint32_t)(m.I * 2), m.I, gate, s0, s1, s2);
+      ok = tile.run(rh, rows_off, rb, bo, (uint32_t)(m.I * 2), m.I, gate, s0, s1, s2,
+                    cdiv(pend - pos0, 16));
     else
       ok = tile.run(rh, rows_off, rb, bo, m.I / kKBlock, gate, reinterpret_cast<float*>(s0));
     if (!ok) return false;
@@ -848,15 +851,19 @@ int launch_moe(const LaunchCommon& lc, const float* logits, const uint16_t* x, i
       reinterpret_cast<const void*>(&moe_kernel<TV_W64>),
       reinterpret_cast<const void*>(&moe_kernel<TV_W128>)};
   const void* k = kernels[tv];
+  constexpr int occ[TV_COUNT] = {MoeCfg<TV_M16>::kOcc, MoeCfg<TV_M32>::kOcc, MoeCfg<TV_M64>::kOcc,
+                                 MoeCfg<TV_W64>::kOcc, MoeCfg<TV_W128>::kOcc};
+  LaunchCommon l = lc;
+  l.G = lc.G * occ[tv];
   if (lc.sched == ET_SCHED_PER_OP) {
     for (int ph = 0; ph < 6; ++ph) {
       ra.phase = ph;
-      int e = lc.launch(k, &ra, &m, false);
+      int e = l.launch(k, &ra, &m, false);
       if (e) return e;
     }
     return ET_OK;
   }
-  return lc.launch(k, &ra, &m, true);
+  return l.launch(k, &ra, &m, true);
 }
 
 }  // namespace et
