@@ -17,8 +17,10 @@ RunArgs LaunchCommon::run_args() const {
   a.hdr = reinterpret_cast<int*>(ws);
   a.counters = reinterpret_cast<int*>(ws + plan->off_counters);
   a.n_events = plan->n_events;
-  a.slots = reinterpret_cast<int*>(ws + plan->off_slots);
+  a.qctl = reinterpret_cast<int*>(ws + plan->off_slots);
+  a.slots = reinterpret_cast<int*>(ws + plan->off_slots + kQCtlBytes);
   a.q_cap = plan->max_tasks;
+  a.nq = shards;
   a.runs = (debug & ET_DEBUG_COUNTS) ? reinterpret_cast<int*>(ws + plan->off_runs) : nullptr;
   a.trace = (debug & ET_DEBUG_TRACE) ? reinterpret_cast<int*>(ws + plan->off_trace) : nullptr;
   a.sched = sched;
@@ -84,6 +86,8 @@ int fill_common(LaunchCommon& lc, void* ws, const et_plan* plan, int sched, cons
   if (o && (o->tile < -1 || o->tile >= TV_COUNT)) return ET_EINVAL;
   lc.coop = o ? o->launch : ET_LAUNCH_ORDINARY;
   if (lc.coop != ET_LAUNCH_ORDINARY && lc.coop != ET_LAUNCH_COOPERATIVE) return ET_EINVAL;
+  lc.shards = o && o->queue_shards ? o->queue_shards : kMaxShards;
+  if (lc.shards != 1 && lc.shards != kMaxShards) return ET_EINVAL;
   lc.stream = stream;
   return workers_for_current_device(&lc.G);
 }
@@ -149,7 +153,7 @@ int et_plan_workspace(int workload, int max_tokens, int hidden, int inter, int n
   plan->off_counters = o;
   o = align_up(o + (size_t)2 * plan->n_events * 4, 256);
   plan->off_slots = o;
-  o = align_up(o + (size_t)plan->max_tasks * 4, 256);
+  o = align_up(o + kQCtlBytes + (size_t)kMaxShards * plan->max_tasks * 4, 256);
   plan->off_runs = o;
   o = align_up(o + (size_t)plan->max_tasks * 4, 256);
   plan->off_trace = o;
@@ -192,6 +196,7 @@ int et_workspace_layout(const et_plan* plan, int n_tokens, et_layout* out) {
     out->inv = b + a.inv;
     out->task_indptr = b + a.task_indptr;
     out->h = b + a.h;
+    out->y = b + a.y;
   }
   (void)n_tokens;
   return ET_OK;
@@ -249,8 +254,16 @@ int et_read_status(const void* ws, const et_plan* plan, hipStream_t stream, et_r
   out->bank = h[HDR_BANK];
   out->calls = h[HDR_CALLS];
   out->last_tasks = h[HDR_LAST_TASKS];
+  int qc[kMaxShards * kQCtlStride];
+  if (hipMemcpy(qc, static_cast<const char*>(ws) + plan->off_slots, sizeof(qc),
+                hipMemcpyDeviceToHost) != hipSuccess)
+    return ET_EHIP;
   out->q_head = h[HDR_QHEAD];
-  out->q_push = h[HDR_QPUSH];
+  out->q_push = 0;
+  for (int q = 0; q < kMaxShards; ++q) {
+    out->q_head += qc[q * kQCtlStride];
+    out->q_push += qc[q * kQCtlStride + 32];
+  }
   out->last_extent = h[HDR_EXT0 + (1 - (h[HDR_BANK] & 1))];
   return ET_OK;
 }

@@ -69,8 +69,10 @@ struct RunArgs {
   int* hdr;            // workspace header words (HDR_*)
   int* counters;       // bank 0; bank 1 starts n_events later
   int n_events;
-  int* slots;          // ready-queue slots (pushed tasks; implicit initial tasks need none)
+  int* qctl;           // ready-queue shard control words (claimed / pushed per shard)
+  int* slots;          // ready-queue slots, [kMaxShards][q_cap] (implicit initial tasks need none)
   int q_cap;
+  int nq;              // ready-queue shards in use (1 or kMaxShards)
   int* runs;           // per-task run counts, or nullptr
   int* trace;          // per-task trace records, or nullptr
   int sched;           // ET_SCHED_*
@@ -83,9 +85,11 @@ struct RunArgs {
   int extent;          // counters this call uses (a prefix of its bank)
 };
 
-// Workgroup-shared scratch for broadcasts.
+// Workgroup-shared scratch for broadcasts and keyed pushes.
 struct Shared {
   int v[8];
+  int qn[kMaxShards];     // push: tasks per shard, then running rank
+  int qb[kMaxShards];     // push: first slot per shard
 };
 
 struct Ctx {
@@ -118,7 +122,7 @@ __device__ __forceinline__ int wg_bcast(const Ctx& c, int v, int slot = 0) {
 
 // Spin (thread 0 only) until counter `idx` of this call's bank reaches
 // -wait_count.  Returns 1, or 0 after a fault (own or another workgroup's).
-__device__ __noinline__ int spin_until(const Ctx& c, int idx, int wait_count, int task) {
+__device__ __forceinline__ int spin_until(const Ctx& c, int idx, int wait_count, int task) {
   const int* p = c.ev + idx;
   const int target = -wait_count;
   int v = ld_rlx(p);
@@ -152,7 +156,7 @@ __device__ __forceinline__ bool wg_wait(const Ctx& c, int idx, int wait_count, i
 
 // Several consecutive events at once (all must fire): the lanes of wave 0
 // check up to 64 counters per memory round trip.
-__device__ __noinline__ int spin_until_all(const Ctx& c, int first, int n, int wait_count,
+__device__ __forceinline__ int spin_until_all(const Ctx& c, int first, int n, int wait_count,
                                            int task) {
   const int lane = threadIdx.x & 63;
   const int target = -wait_count;
@@ -234,22 +238,45 @@ __device__ __forceinline__ void t0_notify(const Ctx& c, int idx, int n, int wait
     __hip_atomic_fetch_add(c.ev + idx, -n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// push(): append tasks id_of(0..n-1) to the ready queue.  Whole workgroup;
-// must follow wg_release() (or a fired wg_notify) so the pushed tasks' inputs
-// are complete before their slots are published.
-template <class F>
-__device__ __forceinline__ void wg_push(const Ctx& c, int n, F id_of) {
+__device__ __forceinline__ int* q_claimed(const RunArgs& a, int q) { return a.qctl + q * kQCtlStride; }
+__device__ __forceinline__ int* q_pushed(const RunArgs& a, int q) {
+  return a.qctl + q * kQCtlStride + 32;
+}
+
+// push(): append tasks id_of(0..n-1) to the ready queue; task i goes to shard
+// key_of(i) mod nq, so tasks with equal keys (those that read the same weight
+// tile) are claimed by workers of one XCD and share its L2.  Whole
+// workgroup; must follow wg_release() (or a fired wg_notify) so the pushed
+// tasks' inputs are complete before their slots are published.  One atomic
+// per shard reserves the slots, then each slot is written; a claimer that
+// finds a reserved slot still empty waits for the write.
+template <class F, class K>
+__device__ __forceinline__ void wg_push(const Ctx& c, int n, F id_of, K key_of) {
   if (n <= 0) return;
-  int base = 0;
-  if (threadIdx.x == 0) base = add_rlx(&c.a.hdr[HDR_QPUSH], n);
-  base = wg_bcast(c, base, 3);
-  for (int i = threadIdx.x; i < n; i += kThreads) {
-    int s = base + i;
+  const int nq = c.a.nq;
+  const int tid = threadIdx.x;
+  if (tid < kMaxShards) c.sh->qn[tid] = 0;
+  __syncthreads();
+  if (nq > 1)
+    for (int i = tid; i < n; i += kThreads) atomicAdd(&c.sh->qn[key_of(i) & (kMaxShards - 1)], 1);
+  else if (tid == 0)
+    c.sh->qn[0] = n;
+  __syncthreads();
+  if (tid < nq) {
+    const int k = c.sh->qn[tid];
+    c.sh->qb[tid] = k ? add_rlx(q_pushed(c.a, tid), k) : 0;
+    c.sh->qn[tid] = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += kThreads) {
+    const int q = nq > 1 ? (key_of(i) & (kMaxShards - 1)) : 0;
+    const int s = c.sh->qb[q] + atomicAdd(&c.sh->qn[q], 1);
     if (s < c.a.q_cap)
-      st_rlx(&c.a.slots[s], id_of(i) + 1);
+      st_rlx(&c.a.slots[(size_t)q * c.a.q_cap + s], id_of(i) + 1);
     else
       raise_fault(c.a, ET_ESTATE, -1, s, c.a.q_cap);
   }
+  __syncthreads();
 }
 
 // Set the total number of tasks of this call (dynamic mode), once known.
@@ -264,59 +291,87 @@ struct PopState {
   int left = 0;
 };
 
-// Thread 0: slot index -> task id, -1 when the call has no more tasks,
-// -2 on a fault.
-__device__ __noinline__ int resolve_slot(const Ctx& c, int idx) {
-  if (idx < c.a.n_init) return idx;
-  const int s = idx - c.a.n_init;
+// Implicit initial tasks of shard q: ids q, q + nq, ... below n_init.
+__device__ __forceinline__ int shard_init(const RunArgs& a, int q) {
+  return a.n_init > q ? (a.n_init - q + a.nq - 1) / a.nq : 0;
+}
+
+// Thread 0: slot index idx of this worker's shard -> task id; -1 when the
+// call has no more tasks for this shard, -2 on a fault.  Index space of a
+// shard: its implicit initial tasks, then its pushed slots.  A claimed slot
+// that is not yet written is waited for; it is given up once every task of
+// the call has been pushed and the index lies beyond what this shard
+// received.
+__device__ __forceinline__ int resolve_slot(const Ctx& c, int q, int idx) {
+  const RunArgs& a = c.a;
+  const int n_init = shard_init(a, q);
+  if (idx < n_init) return q + a.nq * idx;
+  const int s = idx - n_init;
+  int* p = &a.slots[(size_t)q * a.q_cap + s];
   long long t0 = 0;
   for (int it = 0;; ++it) {
-    int total = ld_rlx(&c.a.hdr[HDR_QTOTAL]);
-    if (c.a.total_hint < total) total = c.a.total_hint;
-    if (idx >= total) return -1;
-    if (s < c.a.q_cap) {
-      int v = ld_rlx(&c.a.slots[s]);
+    if (s < a.q_cap) {
+      const int v = ld_rlx(p);
       if (v != 0) {
-        st_rlx(&c.a.slots[s], 0);   // leave the slot empty for the next call
+        st_rlx(p, 0);   // leave the slot empty for the next call
         return v - 1;
+      }
+    }
+    if ((it & 7) == 7) {
+      int total = ld_rlx(&a.hdr[HDR_QTOTAL]);
+      if (a.total_hint < total) total = a.total_hint;
+      if (total != kUnknownTotal) {
+        if (a.nq == 1) {
+          if (idx >= total) return -1;
+        } else {
+          int pushed = 0, mine = 0;
+          for (int j = 0; j < a.nq; ++j) {
+            const int v = ld_rlx(q_pushed(a, j));
+            pushed += v;
+            if (j == q) mine = v;
+          }
+          if (a.n_init + pushed >= total && s >= mine) return -1;
+        }
       }
     }
     if (it == 0) t0 = now_ticks();
     __builtin_amdgcn_s_sleep(1);
     if ((it & 63) == 63) {
-      if (faulted(c.a)) return -2;
-      if (now_ticks() - t0 > c.a.timeout) {
-        raise_fault(c.a, ET_ETIMEOUT, -1, idx, total);
+      if (faulted(a)) return -2;
+      if (now_ticks() - t0 > a.timeout) {
+        raise_fault(a, ET_ETIMEOUT, -1, idx, q);
         return -2;
       }
     }
   }
 }
 
-// pop(): next task of this worker (whole workgroup); claims `fetch` slots
-// per atomic and runs them in slot order (batched fetch, Weave MoE article
-// section 2.2).
+// pop(): next task of this worker (whole workgroup), -1 when there is none
+// left.  The worker takes slots of its own XCD's shard (one shard: a
+// central queue), `fetch` slots per atomic (batched fetch, Weave MoE
+// article section 2.2) but no more than its share of the slots already
+// published beyond the claim counter, so a worker never holds published
+// tasks while others idle; short leading phases are claimed one slot at a
+// time.  A racy peek is enough: any claim size is correct.
 __device__ __forceinline__ int wg_pop(const Ctx& c, PopState& ps) {
   int t = -1;
   if (threadIdx.x == 0) {
+    const RunArgs& a = c.a;
+    const int q = c.wg % a.nq;
     if (ps.left == 0) {
-      // Claim size: up to `fetch` slots per atomic, but no more than this
-      // worker's share of the published (pushed or initial) slots beyond the
-      // claim counter.  A worker then never holds published tasks while
-      // others idle or while it waits for an unpublished slot, and a short
-      // phase of long tasks spreads over all workers.  A racy peek is
-      // enough: any claim size is correct.
-      const int head = ld_rlx(&c.a.hdr[HDR_QHEAD]);
-      const int avail = c.a.n_init + ld_rlx(&c.a.hdr[HDR_QPUSH]) - head;
-      int sz = avail / c.G;
-      sz = head < c.a.n_single ? 1 : (sz < 1 ? 1 : (sz > c.a.fetch ? c.a.fetch : sz));
-      ps.base = add_rlx(&c.a.hdr[HDR_QHEAD], sz);
-      ps.size = sz;
-      ps.left = sz;
+      int* head = q_claimed(a, q);
+      const int h = ld_rlx(head);
+      const int avail = shard_init(a, q) + ld_rlx(q_pushed(a, q)) - h;
+      const int per = c.G / a.nq;
+      int sz = avail / (per > 0 ? per : 1);
+      sz = h * a.nq < a.n_single ? 1 : (sz < 1 ? 1 : (sz > a.fetch ? a.fetch : sz));
+      ps.base = add_rlx(head, sz);
+      ps.size = ps.left = sz;
     }
-    int idx = ps.base + (ps.size - ps.left);
+    const int idx = ps.base + (ps.size - ps.left);
     --ps.left;
-    t = resolve_slot(c, idx);
+    t = resolve_slot(c, q, idx);
+    if (t < 0) t = -1;
   }
   return wg_bcast(c, t, 4);
 }
@@ -376,7 +431,10 @@ __device__ __forceinline__ void epilogue(const Ctx& c, int tasks_this_call) {
       int bank = ld_rlx(&h[HDR_BANK]) & 1;
       st_rlx(&h[HDR_EXIT], 0);
       st_rlx(&h[HDR_QHEAD], 0);
-      st_rlx(&h[HDR_QPUSH], 0);
+      for (int q = 0; q < kMaxShards; ++q) {
+        st_rlx(q_claimed(c.a, q), 0);
+        st_rlx(q_pushed(c.a, q), 0);
+      }
       st_rlx(&h[HDR_QTOTAL], kUnknownTotal);
       st_rlx(&h[HDR_EXT0 + bank], c.a.extent);
       st_rlx(&h[HDR_LAST_TASKS], tasks_this_call);

@@ -19,6 +19,7 @@ struct LaunchCommon {
   int timeout_ms;
   int tile;
   int coop;            // persistent launches: cooperative (1) or ordinary (0)
+  int shards;          // dynamic mode: ready-queue shards (1 or kMaxShards)
   int G;               // workgroups of a persistent launch (one per CU)
   hipStream_t stream;
 

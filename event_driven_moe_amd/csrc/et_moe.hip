@@ -536,7 +536,8 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       // block gb's down tasks: expert e's range, one per column tile
       const int nblk = c_blk[e + 1] - c_blk[e];
       const int b2 = base1 + meta(MD_TOTAL1) + c_blk[e] * nt2 + (gb - c_blk[e]);
-      wg_push(c, nt2, [&](int i) { return b2 + i * nblk; });
+      wg_push(c, nt2, [&](int i) { return b2 + i * nblk; },
+              [&](int i) { return e * nt2 + i; });   // key: the weight tile (e, column tile)
     }
     return true;
   };
@@ -653,7 +654,8 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
         if (sched == ET_SCHED_DYNAMIC) {
           set_total(c, 2 * NR + nb * (nt1 + nt2));
           wg_release();
-          wg_push(c, NR, [&](int i) { return NR + 1 + i; });   // the grouping tasks
+          wg_push(c, NR, [&](int i) { return NR + 1 + i; },    // the grouping tasks
+                  [&](int i) { return i; });
         } else {
           wg_release();
           t0_notify(c, EV_SCAN, 1, 1, NR);
@@ -683,8 +685,18 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
           if (old != 0) raise_fault(ra, ET_ESTATE, NR + 1, m.ev_exp + e, old - n);
         }
       }
-      const int total1 = nb * nt1;
-      wg_push(c, total1, [&](int i) { return base1 + i; });
+      // key of gate/up task i: its weight tile (expert, column tile); the
+      // scan's block offsets per expert are still in LDS
+      const int* blk = reinterpret_cast<const int*>(s1) + 1024;
+      wg_push(c, nb * nt1, [&](int i) { return base1 + i; }, [&](int i) {
+        int lo = 0, hi = m.E;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (blk[mid] * nt1 <= i) lo = mid; else hi = mid;
+        }
+        const int nblk = (lo + 1 < m.E ? blk[lo + 1] : nb) - blk[lo];
+        return lo * nt1 + (i - blk[lo] * nt1) / nblk;
+      });
       return true;
     }
     if (task == NR) {   // the scan as a task of its own: barrier and per-op modes
@@ -727,7 +739,9 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       for (int i = 0; i < nf; ++i) {
         const int e = fe[i];
         const int lo = ld_coh(&m.task_indptr[e]), hi = ld_coh(&m.task_indptr[e + 1]);
-        wg_push(c, hi - lo, [&](int j) { return base1 + lo + j; });
+        const int nblk = (hi - lo) / nt1;
+        wg_push(c, hi - lo, [&](int j) { return base1 + lo + j; },
+                [&](int j) { return e * nt1 + j / nblk; });   // key: (expert, column tile)
       }
       __syncthreads();
       return true;

@@ -30,14 +30,21 @@ enum : int {
   HDR_ERR_A = 65,
   HDR_ERR_B = 66,
   HDR_ERR_C = 67,
-  HDR_QHEAD = 96,       // ready queue: slots claimed
-  HDR_QPUSH = 128,      // ready queue: slots pushed (beyond the implicit initial tasks)
+  HDR_QHEAD = 96,       // ready queue: implicit initial tasks claimed
+  HDR_QPUSH = 128,      // (unused)
   HDR_QTOTAL = 160,     // ready queue: total tasks of this call once known (else INT_MAX)
   HDR_EXIT = 192,       // workgroups that finished this call
   HDR_META = 224,       // 32 words of per-call workload metadata
   HDR_WORDS = 256
 };
 constexpr size_t kHdrBytes = HDR_WORDS * 4;
+
+// Ready-queue shards (dynamic mode): control words of shard q at
+// qctl[q * kQCtlStride] (claimed slots) and qctl[q * kQCtlStride + 32]
+// (pushed slots), each on its own 128-byte line.
+constexpr int kMaxShards = 8;
+constexpr int kQCtlStride = 64;
+constexpr size_t kQCtlBytes = (size_t)kMaxShards * kQCtlStride * 4;
 constexpr int kUnknownTotal = 0x7fffffff;
 
 ET_HD size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kThreads, 1) void splitk_kernel(RunArgs ra, SplitKA
       } else if (sched == ET_SCHED_STATIC) {
         t0_notify(c, i, 1, 4, task);
       } else if (wg_notify(c, i, 1, 4, task)) {
-        wg_push(c, 1, [&](int) { return n1 + i; });   // the zeroing notifier pushes stage-2 i
+        wg_push(c, 1, [&](int) { return n1 + i; }, [&](int) { return i; });   // the zeroing notifier pushes stage-2 i
       }
       return true;
     }

@@ -27,7 +27,7 @@ c_int, c_size_t, c_void_p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 
 class Opts(ctypes.Structure):
     _fields_ = [("fetch_batch", c_int), ("debug_flags", c_int), ("timeout_ms", c_int),
-                ("tile", c_int), ("launch", c_int)]
+                ("tile", c_int), ("launch", c_int), ("queue_shards", c_int)]
 
 
 class Plan(ctypes.Structure):
@@ -44,7 +44,7 @@ class Layout(ctypes.Structure):
                 ("trace", c_size_t),
                 ("topk_ids", c_size_t), ("topk_w", c_size_t), ("counts", c_size_t),
                 ("tok_indptr", c_size_t), ("perm", c_size_t), ("inv", c_size_t),
-                ("task_indptr", c_size_t), ("h", c_size_t)]
+                ("task_indptr", c_size_t), ("h", c_size_t), ("y", c_size_t)]
 
 
 class Report(ctypes.Structure):
@@ -134,9 +134,9 @@ def _ptr(t, dtype, name, shape=None):
 LAUNCH_ORDINARY, LAUNCH_COOPERATIVE = 0, 1
 
 
-def _opts(fetch_batch=4, debug=0, timeout_ms=2000, tile=-1, cooperative=False):
+def _opts(fetch_batch=4, debug=0, timeout_ms=2000, tile=-1, cooperative=False, queue_shards=0):
     return Opts(fetch_batch, debug, timeout_ms, tile,
-                LAUNCH_COOPERATIVE if cooperative else LAUNCH_ORDINARY)
+                LAUNCH_COOPERATIVE if cooperative else LAUNCH_ORDINARY, queue_shards)
 
 
 def plan_workspace(workload, max_tokens, hidden=0, inter=0, n_experts=0, top_k=0):
@@ -245,11 +245,13 @@ def moe_layer(logits, x, w_gate, w_up, w_down, out, ws, sched="dynamic", stream=
                               ctypes.byref(o), _stream(stream)), "et_moe_layer")
 
 
-def moe_aux(ws, T):
-    """Routing results and grouping of the last call (views into the workspace)."""
+def moe_aux(ws, T, intermediates=False):
+    """Routing results and grouping of the last call (views into the workspace);
+    with ``intermediates``, also h (bf16 [T*k, I]) and y (float [T*k, H]), the
+    grouped rows of the two projections."""
     lay = ws.layout(T)
     k, E = ws.plan.top_k, ws.plan.n_experts
-    return {
+    aux = {
         "ids": ws.view(lay.topk_ids, torch.int32, T * k).view(T, k),
         "w": ws.view(lay.topk_w, torch.float32, T * k).view(T, k),
         "counts": ws.view(lay.counts, torch.int32, E),
@@ -258,6 +260,10 @@ def moe_aux(ws, T):
         "inv": ws.view(lay.inv, torch.int32, T * k).view(T, k),
         "task_indptr": ws.view(lay.task_indptr, torch.int32, E + 1),
     }
+    if intermediates:
+        aux["h"] = ws.view(lay.h, torch.bfloat16, T * k * ws.plan.inter).view(T * k, ws.plan.inter)
+        aux["y"] = ws.view(lay.y, torch.float32, T * k * ws.plan.hidden).view(T * k, ws.plan.hidden)
+    return aux
 
 
 def num_workers():

@@ -98,6 +98,10 @@ typedef struct et_opts {
   int timeout_ms;    /* watchdog for every wait / queue spin (default 2000 ms) */
   int tile;          /* MoE / MLP tile-variant override (-1 = chosen from the token count) */
   int launch;        /* ET_LAUNCH_* (default ET_LAUNCH_ORDINARY) */
+  int queue_shards;  /* dynamic mode: ready-queue shards, 1 (one central queue) or 8 (one per
+                        XCD: a pushed task goes to the shard its weight tile hashes to, workers
+                        pop their own XCD's shard first and take from the others when it is
+                        empty); 0 = default (8) */
 } et_opts;
 
 /* Workspace plan: dimensions and byte offsets of every region.  Filled by
@@ -110,7 +114,8 @@ typedef struct et_plan {
   int max_tasks;       /* upper bound of tasks per call (ready-queue capacity) */
   size_t bytes;        /* total workspace bytes */
   size_t off_counters; /* int32 [2][n_events] event counters (two banks) */
-  size_t off_slots;    /* int32 [max_tasks] ready-queue slots */
+  size_t off_slots;    /* ready queue: int32 [8][64] shard control words (claim and push
+                          counters), then int32 [8][max_tasks] slots, one array per shard */
   size_t off_runs;     /* int32 [max_tasks] per-task run counts (ET_DEBUG_COUNTS) */
   size_t off_trace;    /* int32 [max_tasks][4] task trace + [1024][2] workgroup times (ET_DEBUG_TRACE) */
   size_t off_aux;      /* workload intermediates (see et_layout) */
@@ -133,6 +138,7 @@ typedef struct et_layout {
   size_t inv;               /* MoE: int32 [T, k], inv[t, s] = pos */
   size_t task_indptr;       /* MoE: int32 [E+1] gate/up tasks per expert (CSR) */
   size_t h;                 /* MLP: bf16 [B, I]; MoE: bf16 [T*k, I] (grouped rows) */
+  size_t y;                 /* MoE: float [T*k, H] down-projection rows (grouped rows) */
 } et_layout;
 
 /* Device-side state of a workspace, read back by et_read_status(). */
@@ -142,7 +148,8 @@ typedef struct et_report {
   int bank;            /* bank the next call will use */
   int calls;           /* completed calls on this workspace */
   int last_tasks;      /* tasks the last call ran (queue total in dynamic mode) */
-  int q_head, q_push;  /* ready-queue claim and push counters (reset after each call) */
+  int q_head, q_push;  /* ready-queue claim and push counters, summed over the shards
+                          (reset after each call) */
   int last_extent;     /* counters used by the last call */
 } et_report;
 

@@ -199,3 +199,12 @@ def test_cooperative_launch(sched):
     _, _, _, _, out1, aux1, _ = run_moe("moe_skewed", 256, sched, cooperative=True)
     assert np.array_equal(out0, out1)
     check_against_oracle("moe_skewed", 256, out1, aux1)
+
+
+@pytest.mark.parametrize("T", [64, 1024])
+def test_central_queue(T):
+    """One central ready queue instead of one shard per XCD: same results."""
+    _, _, _, _, out8, aux8, _ = run_moe("moe_skewed", T, "dynamic")
+    _, _, _, _, out1, aux1, _ = run_moe("moe_skewed", T, "dynamic", queue_shards=1)
+    assert np.array_equal(out8, out1)
+    check_against_oracle("moe_skewed", T, out1, aux1)

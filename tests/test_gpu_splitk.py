@@ -109,3 +109,11 @@ def test_cooperative_launch(ws, sched):
     assert np.array_equal(B0, B1) and np.array_equal(C0, C1)
     _, Cref = osk.splitk_reduce(A.cpu().numpy())
     assert_rel(C1, Cref, 1e-5, "C")
+
+
+def test_central_queue(ws):
+    """One central ready queue instead of one shard per XCD: same results."""
+    A = synth.splitk_inputs(rows=2048, seed=13, device=DEV)
+    B8, C8 = _run(ws, A, "dynamic")
+    B1, C1 = _run(ws, A, "dynamic", queue_shards=1)
+    assert np.array_equal(C8, C1) and np.array_equal(B8, B1)
