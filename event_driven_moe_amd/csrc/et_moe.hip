@@ -30,9 +30,12 @@
 // tasks[task_indptr[e] : task_indptr[e+1]] (data-dependent fan-out), the one
 // that zeroes EV_H[gb] pushes block gb's down tasks, and the one that zeroes
 // EV_C[t, c] (k down rows of token t for column tile c) runs that combine
-// inline.  Static mode keeps the fine-grained EV_H edge but, as the page's
-// static lowering does for data-dependent edges, replaces EV_EXP by one
-// coarse "all grouped" event and EV_C by one "all down tiles done" event.
+// inline -- in static mode too: EV_C's wait count (k) and index are known
+// statically, only its producers depend on the routing.  Static mode keeps
+// the fine-grained EV_H edge but, as the page's static lowering does for
+// data-dependent edges, replaces EV_EXP by one coarse "all grouped" event.
+// The barrier baseline uses one event per operator throughout, with the
+// combine as tiles of its own after an "all down tiles done" event.
 #include <type_traits>
 
 #include "et_device.hpp"
@@ -69,6 +72,9 @@ struct MoeArgs {
 constexpr int kScanHistBytes = kHistEntries * 4;                    // slot 0
 constexpr int kScanTempBytes = (2 * kMaxExperts + 8 + kThreads) * 4; // slot 1
 constexpr int kGenRowsOff = 0, kGenFired = 512, kGenIdx = 1024;
+// dynamic mode: combine inline in the down tile completing a token's rows
+// (EV_C), or as tiles pushed when the last down tile finishes (EV_DOWN)
+constexpr bool kInlineCombine = false;
 constexpr int kIdxCache = 2 * (kMaxExperts + 1) * 4;   // tok_indptr + blk_indptr copies
 constexpr int kGenBytes = kGenIdx + kIdxCache;
 
@@ -176,6 +182,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   const bool inline_group = (sched == ET_SCHED_STATIC || sched == ET_SCHED_DYNAMIC) &&
                             m.T * m.k <= kInlinePairs;
   const int wc = m.k;   // EV_C wait count: the k rows of a token, one per down column tile
+  const int ncomb = cdiv(m.T, kCombTok) * cdiv(m.H, kCombCols);   // combine tiles
 
   // LDS carve-outs (task kinds never overlap in time inside one workgroup)
   int* s_i = reinterpret_cast<int*>(s0);                              // route / scan / group
@@ -594,11 +601,18 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
           }
     if (sched == ET_SCHED_PER_OP) return true;
     wg_release();
-    if (sched != ET_SCHED_DYNAMIC) {
-      t0_notify(c, EV_DOWN, 1, meta(MD_TOTAL2), task);
+    if (sched != ET_SCHED_DYNAMIC || !kInlineCombine) {
+      if (sched != ET_SCHED_DYNAMIC) {
+        t0_notify(c, EV_DOWN, 1, meta(MD_TOTAL2), task);
+      } else if (wg_notify(c, EV_DOWN, 1, meta(MD_TOTAL2), task)) {
+        // the last down tile: push the combine tiles
+        const int b3 = base1 + meta(MD_TOTAL1) + meta(MD_TOTAL2);
+        wg_push(c, ncomb, [&](int i) { return b3 + i; }, [&](int i) { return i; });
+      }
       return true;
     }
-    // dynamic: one notify per row on EV_C[token, n2]; zeroing rows run the combine
+    // one notify per row on EV_C[token, n2] (wait count k); the notify that
+    // completes a token's k rows for this column tile runs its combine
     if (tid == 0) sh.v[5] = 0;
     __syncthreads();
     if (tid < rows) {
@@ -652,7 +666,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       trace_task(c, NR, ts);
       if (!inline_group) {
         if (sched == ET_SCHED_DYNAMIC) {
-          set_total(c, 2 * NR + nb * (nt1 + nt2));
+          set_total(c, 2 * NR + nb * (nt1 + nt2) + (kInlineCombine ? 0 : ncomb));
           wg_release();
           wg_push(c, NR, [&](int i) { return NR + 1 + i; },    // the grouping tasks
                   [&](int i) { return i; });
@@ -677,7 +691,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       // dynamic: every expert event receives all of its rows at once (its
       // data-dependent wait count) and fires; the fired experts' task ranges
       // together are the whole gate/up range, pushed in one piece
-      set_total(c, NR + nb * (nt1 + nt2));
+      set_total(c, NR + nb * (nt1 + nt2) + (kInlineCombine ? 0 : ncomb));
       for (int e = tid; e < m.E; e += kThreads) {
         const int n = ld_coh(&m.counts[e]);
         if (n > 0) {
@@ -752,7 +766,6 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     return combine_tile(task - base1 - total1 - total2, task);
   };
 
-  const int ncomb = cdiv(m.T, kCombTok) * cdiv(m.H, kCombCols);
   if (sched == ET_SCHED_DYNAMIC) {
     PopState ps;
     for (;;) {

@@ -116,13 +116,13 @@ struct MlpPlan {
 //   EV_SCAN   scan done                   (1)
 //   EV_GROUP  all grouping tasks done     (n_route)
 //   EV_G1ALL  all gate/up tasks done      (total1)        [barrier mode]
-//   EV_DOWN   all down tasks done         (total2)        [static / barrier]
+//   EV_DOWN   all down tasks done         (total2)        [barrier]
 //   EV_EXP[e] rows of expert e grouped    (counts[e])     data-dependent
 //   EV_H[gb]  gate/up tiles of block gb   (inter / bn1)
-//   EV_C[t][c] down tiles covering token t, column tile c (top_k) [dynamic]
+//   EV_C[t][c] down tiles covering token t, column tile c (top_k) [static, dynamic]
 // tasks: [0, R) routing, R scan, [R+1, 2R+1) grouping, then total1 gate/up
-//   tiles (block-major, column tile fastest), total2 down tiles, then (static,
-//   barrier, per-op) combine tiles of kCombTok tokens x kCombCols columns.
+//   tiles (block-major, column tile fastest), total2 down tiles, then (barrier,
+//   per-op) combine tiles of kCombTok tokens x kCombCols columns.
 // ---------------------------------------------------------------------------
 constexpr int kCombTok = 16;
 constexpr int kCombCols = 256;
