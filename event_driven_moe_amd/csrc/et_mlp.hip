@@ -149,14 +149,11 @@ __global__ __launch_bounds__(kThreads, kMlpOcc<MT>) void mlp_kernel(RunArgs ra, 
       trace_task(c, t, t0);
     }
   } else {
+    // one round-robin over all tasks (gate/up ids first): the down tiles land
+    // on the workgroups with the fewest gate/up tiles, and every workgroup
+    // finishes its gate/up tiles before it waits in a down tile
     bool ok = true;
-    for (int t = c.wg; ok && t < n_gate; t += c.G) {
-      const long long t0 = trace_now(c);
-      ok = run(t);
-      if (ok) count_run(c, t);
-      if (ok) trace_task(c, t, t0);
-    }
-    for (int t = n_gate + c.wg; ok && t < total; t += c.G) {
+    for (int t = c.wg; ok && t < total; t += c.G) {
       const long long t0 = trace_now(c);
       ok = run(t);
       if (ok) count_run(c, t);
