@@ -489,6 +489,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// Sum over each 16-lane row, result in every lane of the row (quad
+// permutes, then the half-row and row mirrors).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_f32<0xB1>(x);    // quad [1,0,3,2]
+  x += dpp_f32<0x4E>(x);    // quad [2,3,0,1]
+  x += dpp_f32<0x141>(x);   // row half mirror
+  x += dpp_f32<0x140>(x);   // row mirror
+  return x;
+}
+
 // Wave-wide unsigned max / min through DPP lane moves (no LDS round trips):
 // quad permutes and row mirrors reduce each 16-lane row, two row broadcasts
 // fold the rows into lane 63, which is read back as a uniform value.

@@ -226,8 +226,8 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   // [c0, c0 + ncols): out[t, col] = sum_{s<k} w[t, s] * y[inv[t, s], col],
   // accumulated in slot order with one fused multiply-add per slot.  The
   // (w, position) pairs are staged in LDS first; each thread then owns 4
-  // columns and issues its k 16-byte row loads before summing, so a pass
-  // costs two memory round trips.  The dynamic (inline) and tiled (static)
+  // columns of one or two items and issues all their 16-byte row loads
+  // before summing, so a pass costs one memory round trip.  The dynamic (inline) and tiled (static)
   // combines share this code and give bit-identical results.
   auto combine = [&](int ntok, auto tok_of, int c0, int ncols, float* cw, int* cp) ET_INLINE {
     const int k = m.k;
@@ -238,25 +238,44 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     }
     __syncthreads();
     const int nq = ncols / 4;              // 4 columns (16 bytes) per item
-    for (int i = tid; i < ntok * nq; i += kThreads) {
-      const int ti = i / nq, col = c0 + 4 * (i % nq);
-      i32x4 yv[kMaxTopK];
+    const int nit = ntok * nq;
+    // IT items per thread per pass, all KM * IT row loads issued before any
+    // sum (IT = 2 when k <= 8 keeps the loads within 64 registers)
+    auto pass = [&](auto km_c, auto it_c) ET_INLINE {
+      constexpr int KM = decltype(km_c)::value, IT = decltype(it_c)::value;
+      for (int i0 = tid; i0 < nit; i0 += IT * kThreads) {
+        i32x4 yv[IT][KM];
 #pragma unroll
-      for (int s = 0; s < kMaxTopK; ++s)
-        if (s < k) yv[s] = ld16c(ry, (uint32_t)((cp[ti * k + s] * (size_t)m.H + col) * 4));
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int u = 0; u < IT; ++u) {
+          const int i = i0 + u * kThreads;
+          const int ti = i / nq, col = c0 + 4 * (i % nq);
 #pragma unroll
-      for (int s = 0; s < kMaxTopK; ++s)
-        if (s < k) {
-          const float w = cw[ti * k + s];
-          const f32x4 y4 = __builtin_bit_cast(f32x4, yv[s]);
-          acc.x = __fmaf_rn(w, y4[0], acc.x);
-          acc.y = __fmaf_rn(w, y4[1], acc.y);
-          acc.z = __fmaf_rn(w, y4[2], acc.z);
-          acc.w = __fmaf_rn(w, y4[3], acc.w);
+          for (int s = 0; s < KM; ++s)
+            if (s < k && i < nit) yv[u][s] = ld16c(ry, (uint32_t)((cp[ti * k + s] * (size_t)m.H + col) * 4));
         }
-      *reinterpret_cast<float4*>(m.out + (size_t)tok_of(ti) * m.H + col) = acc;
-    }
+#pragma unroll
+        for (int u = 0; u < IT; ++u) {
+          const int i = i0 + u * kThreads;
+          if (i >= nit) break;
+          const int ti = i / nq, col = c0 + 4 * (i % nq);
+          float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+          for (int s = 0; s < KM; ++s)
+            if (s < k) {
+              const float w = cw[ti * k + s];
+              const f32x4 y4 = __builtin_bit_cast(f32x4, yv[u][s]);
+              acc.x = __fmaf_rn(w, y4[0], acc.x);
+              acc.y = __fmaf_rn(w, y4[1], acc.y);
+              acc.z = __fmaf_rn(w, y4[2], acc.z);
+              acc.w = __fmaf_rn(w, y4[3], acc.w);
+            }
+          *reinterpret_cast<float4*>(m.out + (size_t)tok_of(ti) * m.H + col) = acc;
+        }
+      }
+    };
+    using std::integral_constant;
+    if (k <= 8) pass(integral_constant<int, 8>{}, integral_constant<int, 2>{});
+    else pass(integral_constant<int, kMaxTopK>{}, integral_constant<int, 1>{});
     __syncthreads();
   };
   // static / barrier: coarse events already seen fired by this workgroup
@@ -289,39 +308,56 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
             kb[b][j] = (t < t1 && e < m.E) ? route_key32(lg[e]) : 0u;   // 0: below every key
           }
         }
+        // the NB tokens' k rounds are interleaved: their wave reductions are
+        // independent chains that the scheduler overlaps
+        uint32_t taken[NB], my_key[NB], key0[NB];
+        int my_e[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          taken[b] = 0;   // bit j: my expert lane + 64 j already chosen
+          my_e[b] = -1;
+          my_key[b] = key0[b] = 0;
+        }
+        for (int s = 0; s < m.k; ++s) {
+          uint32_t best[NB], top[NB];
+          int best_e[NB], e[NB];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            best[b] = 0;
+            best_e[b] = 0x7fffffff;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+              const bool ok = !((taken[b] >> j) & 1u) && lane + 64 * j < m.E;
+              if (ok && kb[b][j] > best[b]) {   // strict: equal keys keep the lower expert
+                best[b] = kb[b][j];
+                best_e[b] = lane + 64 * j;
+              }
+            }
+          }
+#pragma unroll
+          for (int b = 0; b < NB; ++b) top[b] = wave_reduce_u32<true>(best[b]);
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            e[b] = (int)wave_reduce_u32<false>(best[b] == top[b] ? (uint32_t)best_e[b] : 0xffffffffu);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            if (s == 0) key0[b] = top[b];
+            if (lane == s) { my_e[b] = e[b]; my_key[b] = top[b]; }
+            if ((e[b] & 63) == lane) taken[b] |= 1u << (e[b] >> 6);
+          }
+        }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
           const int t = tb + 4 * b;
           if (t >= t1) break;
-          uint32_t taken = 0;                // bit j: my expert lane + 64 j already chosen
-          int my_e = -1;
-          uint32_t my_key = 0, key0 = 0;
-          for (int s = 0; s < m.k; ++s) {
-            uint32_t best = 0;
-            int best_e = 0x7fffffff;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-              const bool ok = !((taken >> j) & 1u) && lane + 64 * j < m.E;
-              if (ok && kb[b][j] > best) {   // strict: equal keys keep the lower expert
-                best = kb[b][j];
-                best_e = lane + 64 * j;
-              }
-            }
-            const uint32_t top = wave_reduce_u32<true>(best);
-            const int e = (int)wave_reduce_u32<false>(best == top ? (uint32_t)best_e : 0xffffffffu);
-            if (s == 0) key0 = top;
-            if (lane == s) { my_e = e; my_key = top; }
-            if ((e & 63) == lane) taken |= 1u << (e >> 6);
-          }
-          // weights: softmax over the kept logits (= renormalised top-k softmax)
-          const float ex = lane < m.k ? expf(key_to_float(my_key) - key_to_float(key0)) : 0.f;
-          float sum = ex;
-#pragma unroll
-          for (int d = 1; d < 64; d <<= 1) sum += __shfl_xor(sum, d);
+          // weights: softmax over the kept logits (= renormalised top-k
+          // softmax); lanes 0..k-1 of row 0 hold them, summed within the row
+          const float ex = lane < m.k ? expf(key_to_float(my_key[b]) - key_to_float(key0[b])) : 0.f;
+          const float sum = row_sum16(ex);
           if (lane < m.k) {
-            st_coh(&m.topk_ids[t * m.k + lane], my_e);
+            st_coh(&m.topk_ids[t * m.k + lane], my_e[b]);
             st_coh(&m.topk_w[t * m.k + lane], ex / sum);
-            atomicAdd(&hist_l[my_e], 1);
+            atomicAdd(&hist_l[my_e[b]], 1);
           }
         }
       }
