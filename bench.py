@@ -300,7 +300,7 @@ def main():
             "algorithmic_bytes": alg["bytes"], "flops": alg["flops"],
             "mfma_frac": round(achieved_tfs / MFMA_BF16_PEAK_TFS, 4),
             "hbm_frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
-            "kernel": "moe_kernel (one persistent cooperative launch per layer)",
+            "kernel": "moe_kernel (one persistent launch per layer)",
         },
         "roofline": roof,
     }
