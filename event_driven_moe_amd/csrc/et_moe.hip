@@ -64,6 +64,7 @@ struct MoeArgs {
   uint16_t* h;
   float* y;
   int T, H, I, E, k, NR, tpr;
+  int ccols;           // combine tile columns
   int ev_exp, ev_h, ev_c;
 };
 
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   const bool inline_group = (sched == ET_SCHED_STATIC || sched == ET_SCHED_DYNAMIC) &&
                             m.T * m.k <= kInlinePairs;
   const int wc = m.k;   // EV_C wait count: the k rows of a token, one per down column tile
-  const int ncomb = cdiv(m.T, kCombTok) * cdiv(m.H, kCombCols);   // combine tiles
+  const int ncomb = cdiv(m.T, kCombTok) * cdiv(m.H, m.ccols);   // combine tiles
 
   // LDS carve-outs (task kinds never overlap in time inside one workgroup)
   int* s_i = reinterpret_cast<int*>(s0);                              // route / scan / group
@@ -674,12 +675,12 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       if (!wg_wait(c, EV_DOWN, meta(MD_TOTAL2), task)) return false;
       seen_down = true;
     }
-    const int ncol = cdiv(m.H, kCombCols);
+    const int ncol = cdiv(m.H, m.ccols);
     const int tc = t3 / ncol, cc = t3 % ncol;
     const int t0 = tc * kCombTok;
     const int ntok = min(m.T, t0 + kCombTok) - t0;
-    const int c0 = cc * kCombCols;
-    combine(ntok, [&](int i) { return t0 + i; }, c0, min(kCombCols, m.H - c0),
+    const int c0 = cc * m.ccols;
+    combine(ntok, [&](int i) { return t0 + i; }, c0, min(m.ccols, m.H - c0),
             reinterpret_cast<float*>(s0), reinterpret_cast<int*>(s0) + kMaxTopK * 128);
     return true;
   };
@@ -712,6 +713,10 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
         }
         return true;
       }
+      if (sched == ET_SCHED_STATIC) {   // tasks may start and prefetch weights while grouping runs
+        wg_release();
+        t0_notify(c, EV_SCAN, 1, 1, NR);
+      }
       ts = trace_now(c);
       group_inline();
       for (int r = 0; r < NR; ++r) {
@@ -720,7 +725,6 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       }
       wg_release();
       if (sched == ET_SCHED_STATIC) {
-        t0_notify(c, EV_SCAN, 1, 1, NR);
         t0_notify(c, EV_GROUP, NR, NR, NR + 1);
         return true;
       }
@@ -899,6 +903,9 @@ int launch_moe(const LaunchCommon& lc, const float* logits, const uint16_t* x, i
   m.k = p->top_k;
   m.NR = mp.routes(T);
   m.tpr = mp.tpr(T);
+  // combine tiles: 16 tokens x 256 columns, or x 64 columns when that leaves
+  // workgroups without a tile
+  m.ccols = cdiv(T, kCombTok) * cdiv(m.H, kCombCols) >= lc.G ? kCombCols : kCombColsMin;
   m.ev_exp = mp.ev_exp();
   m.ev_h = mp.ev_h();
   m.ev_c = mp.ev_c();

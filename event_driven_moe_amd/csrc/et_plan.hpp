@@ -125,7 +125,8 @@ struct MlpPlan {
 //   per-op) combine tiles of kCombTok tokens x kCombCols columns.
 // ---------------------------------------------------------------------------
 constexpr int kCombTok = 16;
-constexpr int kCombCols = 256;
+constexpr int kCombCols = 256;      // combine tile columns (64 when 256 gives fewer tiles than CUs)
+constexpr int kCombColsMin = 64;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kHistEntries = 8192;    // n_route * E must fit (int32, 32 KB of LDS)
@@ -145,7 +146,7 @@ struct MoePlan {
   ET_HD int ev_c() const { return ev_h() + nb_max(); }
   ET_HD int n_events_max() const { return ev_c() + t_max * (hidden / kMinCols); }
   ET_HD int extent(int T, const Tiling& t) const { return ev_c() + T * (hidden / t.bn2); }
-  ET_HD int n_comb(int T) const { return cdiv(T, kCombTok) * cdiv(hidden, kCombCols); }
+  ET_HD int n_comb(int T) const { return cdiv(T, kCombTok) * cdiv(hidden, kCombColsMin); }
   ET_HD int max_tasks() const {
     return 2 * n_route + 1 + nb_max() * (inter / kMinCols + hidden / kMinCols) + n_comb(t_max);
   }

@@ -112,7 +112,8 @@ def test_event_invariants(sched, T):
     nr = min(128, 8192 // E, -(-T // 8))   # routing chunks of about 8 tokens
     rows, bn1, bn2 = moe_tiling(T, k)
     tab = oev.moe_table(aux["counts"], rows, I, bn1, H, bn2, nr)
-    ncomb = -(-T // 16) * -(-H // 256)     # combine tiles of 16 tokens x 256 columns
+    ccols = 256 if -(-T // 16) * -(-H // 256) >= et.num_workers() else 64
+    ncomb = -(-T // 16) * -(-H // ccols)   # combine tiles of 16 tokens x ccols columns
     total = sum(tab["tasks"].values()) + ncomb
     runs = ws.runs().cpu().numpy()
     assert (runs[:total] == 1).all() and (runs[total:] == 0).all()
