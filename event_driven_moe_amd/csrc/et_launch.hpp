@@ -63,8 +63,7 @@ inline int pick_mlp_tile(int batch, int forced) {
 inline int pick_moe_tile(int tokens, int top_k, int n_experts, int forced) {
   if (forced >= 0 && forced < TV_COUNT) return forced;
   (void)n_experts;
-  if (tokens <= 16) return TV_M16;
-  if (tokens <= 32) return TV_M32;
+  if (tokens <= 32) return TV_M16;
   if (tokens * top_k <= 256) return TV_M64;
   if (tokens <= 512) return TV_W64;
   return TV_W128;

@@ -77,8 +77,7 @@ def moe_tiling(T, k, tile=-1):
     """(rows per block, h columns per gate/up task, columns per down task) of
     the library's tile variant for T tokens routed to k experts each (or the
     forced variant)."""
-    tv = tile if tile >= 0 else (0 if T <= 16 else 1 if T <= 32 else 2 if T * k <= 256 else
-                                 3 if T <= 512 else 4)
+    tv = tile if tile >= 0 else (0 if T <= 32 else 2 if T * k <= 256 else 3 if T <= 512 else 4)
     return {0: (16, 16, 16), 1: (32, 16, 16), 2: (64, 16, 16), 3: (64, 128, 256),
             4: (128, 128, 256)}[tv]
 
