@@ -63,7 +63,10 @@ inline int pick_mlp_tile(int batch, int forced) {
 inline int pick_moe_tile(int tokens, int top_k, int n_experts, int forced) {
   if (forced >= 0 && forced < TV_COUNT) return forced;
   (void)n_experts;
-  if (tokens <= 32) return TV_M16;
+  // 64-column down tasks once 16 or more (token, expert) pairs are routed
+  // (typically 8+ row blocks, so 256+ such tasks); with fewer rows the
+  // 16-column ones keep every CU busy
+  if (tokens <= 32) return tokens * top_k >= 16 ? TV_M16W : TV_M16;
   if (tokens * top_k <= 256) return TV_M64;
   if (tokens <= 512) return TV_W64;
   return TV_W128;

@@ -134,16 +134,17 @@ struct MoeCfg {
   static constexpr int MT = t.mt;
   static constexpr bool kWide = TV == TV_W64 || TV == TV_W128;
   static constexpr int NH = kWide ? 2 : 1;          // 16-column h groups per wave (gate/up)
-  static constexpr int NB2 = kWide ? 4 : 1;         // 16-column groups per wave (down)
+  static constexpr int NB2 = t.bn2 == 16 ? 1 : 4;   // 16-column groups per wave (down)
   static constexpr int PD = MT == 1 ? 4 : (MT == 2 ? 3 : 2);
+  static constexpr int PD2 = NB2 == 4 ? 2 : PD;     // down tiles: K-blocks in flight
   static constexpr int kOcc = 1;                    // workgroups per CU
 };
 
-template <int TV, bool COH, int NB>
+template <int TV, bool COH, int NB, int PDX>
 struct TileOf {
   using type = typename std::conditional<
       MoeCfg<TV>::kWide, RingTile<MoeCfg<TV>::MT, COH>,
-      StreamTile<MoeCfg<TV>::MT, NB, 4, MoeCfg<TV>::PD, COH>>::type;
+      StreamTile<MoeCfg<TV>::MT, NB, 4, PDX, COH>>::type;
 };
 
 template <int A, int B>
@@ -159,15 +160,16 @@ __device__ __forceinline__ int xcd_pos(int w, int G) {
 template <int TV>
 __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs ra, MoeArgs m) {
   using Cfg = MoeCfg<TV>;
-  using Tile1 = typename TileOf<TV, false, 2 * Cfg::NH>::type;   // gate/up: reads x
-  using Tile2 = typename TileOf<TV, true, Cfg::NB2>::type;       // down: reads h (this launch)
+  using Tile1 = typename TileOf<TV, false, 2 * Cfg::NH, Cfg::PD>::type;   // gate/up: reads x
+  using Tile2 = typename TileOf<TV, true, Cfg::NB2, Cfg::PD2>::type;      // down: reads h (this launch)
   constexpr int MT = Cfg::MT;
   constexpr bool kWide = Cfg::kWide;
   constexpr int bn1 = Cfg::t.bn1, bn2 = Cfg::t.bn2;
   constexpr int kSlot = kWide ? Tile1::kStageBytes : 0;
   __shared__ Shared sh;
   __shared__ __align__(16) unsigned char gen[kGenBytes];
-  __shared__ __align__(16) unsigned char s0[cmax<cmax<kSlot, kScanHistBytes>(), Tile1::kLdsBytes>()];
+  __shared__ __align__(16) unsigned char s0[cmax<cmax<kSlot, kScanHistBytes>(),
+                                                 cmax<Tile1::kLdsBytes, Tile2::kLdsBytes>()>()];
   __shared__ __align__(16) unsigned char s1[cmax<kSlot, kScanTempBytes>()];
   __shared__ __align__(16) unsigned char s2[cmax<kSlot, 16>()];
 
@@ -919,10 +921,12 @@ int launch_moe(const LaunchCommon& lc, const float* logits, const uint16_t* x, i
       reinterpret_cast<const void*>(&moe_kernel<TV_M32>),
       reinterpret_cast<const void*>(&moe_kernel<TV_M64>),
       reinterpret_cast<const void*>(&moe_kernel<TV_W64>),
-      reinterpret_cast<const void*>(&moe_kernel<TV_W128>)};
+      reinterpret_cast<const void*>(&moe_kernel<TV_W128>),
+      reinterpret_cast<const void*>(&moe_kernel<TV_M16W>)};
   const void* k = kernels[tv];
   constexpr int occ[TV_COUNT] = {MoeCfg<TV_M16>::kOcc, MoeCfg<TV_M32>::kOcc, MoeCfg<TV_M64>::kOcc,
-                                 MoeCfg<TV_W64>::kOcc, MoeCfg<TV_W128>::kOcc};
+                                 MoeCfg<TV_W64>::kOcc, MoeCfg<TV_W128>::kOcc,
+                                 MoeCfg<TV_M16W>::kOcc};
   LaunchCommon l = lc;
   l.G = lc.G * occ[tv];
   if (lc.sched == ET_SCHED_PER_OP) {

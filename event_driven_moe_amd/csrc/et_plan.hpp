@@ -70,12 +70,15 @@ struct Tiling {
 // busy; the wide variants (64 / 128 rows, 128 h columns per gate/up task and
 // 256 output columns per down task) serve many rows, where MFMA throughput
 // and operand reuse matter.
-enum : int { TV_M16 = 0, TV_M32 = 1, TV_M64 = 2, TV_W64 = 3, TV_W128 = 4, TV_COUNT = 5 };
+// TV_M16W: 16 rows, 16-column gate/up tasks, 64-column down tasks (fewer,
+// longer down tasks whose weight stream is mostly fetched before their h
+// block is ready; used when there are enough row blocks to fill the CUs).
+enum : int { TV_M16 = 0, TV_M32 = 1, TV_M64 = 2, TV_W64 = 3, TV_W128 = 4, TV_M16W = 5, TV_COUNT = 6 };
 
 __host__ __device__ constexpr Tiling tiling_of(int tv) {
-  return Tiling{tv == TV_M16 ? 1 : (tv == TV_M32 ? 2 : (tv == TV_W128 ? 8 : 4)),
+  return Tiling{(tv == TV_M16 || tv == TV_M16W) ? 1 : (tv == TV_M32 ? 2 : (tv == TV_W128 ? 8 : 4)),
                 (tv == TV_W64 || tv == TV_W128) ? 128 : 16,
-                (tv == TV_W64 || tv == TV_W128) ? 256 : 16};
+                (tv == TV_W64 || tv == TV_W128) ? 256 : (tv == TV_M16W ? 64 : 16)};
 }
 constexpr int kMinRows = 16;       // smallest rows per tile over all variants
 constexpr int kMinCols = 16;       // smallest bn1 / bn2 over all variants

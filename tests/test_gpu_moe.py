@@ -77,13 +77,14 @@ def moe_tiling(T, k, tile=-1):
     """(rows per block, h columns per gate/up task, columns per down task) of
     the library's tile variant for T tokens routed to k experts each (or the
     forced variant)."""
-    tv = tile if tile >= 0 else (0 if T <= 32 else 2 if T * k <= 256 else 3 if T <= 512 else 4)
+    tv = tile if tile >= 0 else ((5 if T * k >= 16 else 0) if T <= 32 else 2 if T * k <= 256 else
+                                 3 if T <= 512 else 4)
     return {0: (16, 16, 16), 1: (32, 16, 16), 2: (64, 16, 16), 3: (64, 128, 256),
-            4: (128, 128, 256)}[tv]
+            4: (128, 128, 256), 5: (16, 16, 64)}[tv]
 
 
 @pytest.mark.parametrize("sched", ["static", "dynamic"])
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("T", [64, 1024])
 def test_tile_variants(tile, sched, T):
     _, _, _, _, out, aux, _ = run_moe("moe_skewed", T, sched, tile=tile)
