@@ -504,6 +504,23 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: shifts of 1, 2, 4, 8
+// within each 16-lane row, then the row totals carried across rows by the
+// two row broadcasts (rows 1, 3 from lanes 15, 47; rows 2, 3 from lane 31).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_i32<0x111, 0xf>(x);   // row_shr:1
+  x += dpp_i32<0x112, 0xf>(x);   // row_shr:2
+  x += dpp_i32<0x114, 0xf>(x);   // row_shr:4
+  x += dpp_i32<0x118, 0xf>(x);   // row_shr:8
+  x += dpp_i32<0x142, 0xa>(x);   // row_bcast:15 into rows 1, 3
+  x += dpp_i32<0x143, 0xc>(x);   // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // Wave-wide unsigned max / min through DPP lane moves (no LDS round trips):
 // quad permutes and row mirrors reduce each 16-lane row, two row broadcasts
 // fold the rows into lane 63, which is read back as a uniform value.

@@ -83,7 +83,7 @@ constexpr int kGenBytes = kGenIdx + kIdxCache;
 // block-wide exclusive scan of n <= 1024 ints held in LDS (in place);
 // returns the total.  256 threads, 4 consecutive elements per thread.
 // ---------------------------------------------------------------------------
-__device__ int block_exscan(int* a, int n, int* tmp /* >= 8 ints */) {
+__device__ __forceinline__ int block_exscan(int* a, int n, int* tmp /* >= 8 ints */) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   int v[4], s = 0;
 #pragma unroll
@@ -92,12 +92,7 @@ __device__ int block_exscan(int* a, int n, int* tmp /* >= 8 ints */) {
     v[i] = j < n ? a[j] : 0;
     s += v[i];
   }
-  int inc = s;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(inc, d);
-    if (lane >= d) inc += o;
-  }
+  const int inc = wave_incl_scan(s);
   if (lane == 63) tmp[wave] = inc;
   __syncthreads();
   int wbase = 0;
@@ -399,8 +394,10 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     }
     __syncthreads();
     // per-expert prefix over the chunks r: P threads per expert, each summing
-    // a contiguous range of r, then the P partial sums in order
-    const int P = m.E >= kThreads ? 1 : kThreads / m.E;
+    // a contiguous range of about 4 or more chunks, then the P partial sums
+    // in order
+    int P = m.E >= kThreads ? 1 : kThreads / m.E;
+    P = min(P, cdiv(n_ne, 4));
     const int span = cdiv(n_ne, P);
     for (int q = tid; q < m.E * P; q += kThreads) {
       const int e = q / P, p = q % P;
