@@ -555,20 +555,49 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     else
       ok = tile.run(rx, rows_off, rb, bo, m.H / kKBlock, gate, reinterpret_cast<float*>(s0));
     if (!ok) return false;
+    if constexpr (kWide) {
+      // h = SiLU(g) * u staged as a bf16 tile in the (now idle) ring slot,
+      // then written out with 16-byte coherent stores, 16 per 128-column row
+      constexpr int kHs = bn1 + 8;                 // padded row (elements)
+      uint16_t* hl = reinterpret_cast<uint16_t*>(s0);
+      const int nrow = pend - pos0;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
+        if (16 * mt < nrow) {
 #pragma unroll
-      for (int j = 0; j < Cfg::NH; ++j)
+          for (int j = 0; j < Cfg::NH; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (kWide || r == wave) {
-            const int pos = pos0 + 16 * mt + 4 * (lane >> 4) + r;
-            if (pos < pend) {
+            for (int r = 0; r < 4; ++r) {
               const float g = tile.acc[mt][j][r], u = tile.acc[mt][Cfg::NH + j][r];
-              st_coh(&m.h[(size_t)pos * m.I + n * bn1 + cw + 16 * j + (lane & 15)],
-                     f32_to_bf16(silu(g) * u));
+              hl[(16 * mt + 4 * (lane >> 4) + r) * kHs + cw + 16 * j + (lane & 15)] =
+                  f32_to_bf16(silu(g) * u);
             }
-          }
+        }
+      __syncthreads();
+      const Rsrc rh = make_rsrc(m.h, (uint32_t)m.T * m.k * m.I * 2);
+      constexpr int kCpr = bn1 / 8;                // 16-byte chunks per row
+      for (int i = tid; i < nrow * kCpr; i += kThreads) {
+        const int row = i / kCpr, ch = i % kCpr;
+        st16c(rh, (uint32_t)((pos0 + row) * m.I + n * bn1 + 8 * ch) * 2u,
+              *reinterpret_cast<const i32x4*>(hl + row * kHs + 8 * ch));
+      }
+      __syncthreads();   // the ring slot is refilled by the next task
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < Cfg::NH; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (r == wave) {
+              const int pos = pos0 + 16 * mt + 4 * (lane >> 4) + r;
+              if (pos < pend) {
+                const float g = tile.acc[mt][j][r], u = tile.acc[mt][Cfg::NH + j][r];
+                st_coh(&m.h[(size_t)pos * m.I + n * bn1 + cw + 16 * j + (lane & 15)],
+                       f32_to_bf16(silu(g) * u));
+              }
+            }
+    }
     if (sched == ET_SCHED_PER_OP) return true;
     wg_release();
     if (sched == ET_SCHED_BARRIER) {
@@ -624,17 +653,46 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     else
       ok = tile.run(rh, rows_off, rb, bo, m.I / kKBlock, gate, reinterpret_cast<float*>(s0));
     if (!ok) return false;
+    if constexpr (kWide) {
+      // y staged 32 rows at a time in the (now idle) ring slot, then written
+      // out with 16-byte coherent stores, 64 per 256-column row
+      constexpr int kYs = bn2 + 4;                 // padded row (floats)
+      float* yl = reinterpret_cast<float*>(s0);
+      const int nrow = pend - pos0;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int q = 0; q < MT / 2; ++q)
+        if (32 * q < nrow) {
 #pragma unroll
-      for (int j = 0; j < Cfg::NB2; ++j)
+          for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (kWide || r == wave) {
-            const int pos = pos0 + 16 * mt + 4 * (lane >> 4) + r;
-            if (pos < pend)
-              st_coh(&m.y[(size_t)pos * m.H + n2 * bn2 + cw + 16 * j + (lane & 15)], tile.acc[mt][j][r]);
+            for (int j = 0; j < Cfg::NB2; ++j)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                yl[(16 * mm + 4 * (lane >> 4) + r) * kYs + cw + 16 * j + (lane & 15)] =
+                    tile.acc[2 * q + mm][j][r];
+          __syncthreads();
+          const int nr = min(32, nrow - 32 * q);
+          constexpr int kCpr = bn2 / 4;            // 16-byte chunks per row
+          for (int i = tid; i < nr * kCpr; i += kThreads) {
+            const int row = i / kCpr, ch = i % kCpr;
+            st16c(ry, (uint32_t)((pos0 + 32 * q + row) * m.H + n2 * bn2 + 4 * ch) * 4u,
+                  *reinterpret_cast<const i32x4*>(yl + row * kYs + 4 * ch));
           }
+          __syncthreads();
+        }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < Cfg::NB2; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (r == wave) {
+              const int pos = pos0 + 16 * mt + 4 * (lane >> 4) + r;
+              if (pos < pend)
+                st_coh(&m.y[(size_t)pos * m.H + n2 * bn2 + cw + 16 * j + (lane & 15)], tile.acc[mt][j][r]);
+            }
+    }
     if (sched == ET_SCHED_PER_OP) return true;
     wg_release();
     if (sched != ET_SCHED_DYNAMIC || !kInlineCombine) {
