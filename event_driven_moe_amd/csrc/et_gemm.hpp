@@ -156,6 +156,12 @@ __device__ __forceinline__ void dma16(Rsrc r, void* lds_base, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ET_LDS_PTR(lds_base), 16, voff, 0, 0, COH ? 16 : 0);
 }
 
+// Workgroup barrier that waits for this wave's LDS accesses only (the
+// compiler's __syncthreads also waits for every outstanding global store).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Wait until at most N of this wave's memory loads are outstanding, then the
 // workgroup barrier (a compiler memory barrier too).
 template <int N>

@@ -573,7 +573,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
                   f32_to_bf16(silu(g) * u);
             }
         }
-      __syncthreads();
+      lds_barrier();
       const Rsrc rh = make_rsrc(m.h, (uint32_t)m.T * m.k * m.I * 2);
       constexpr int kCpr = bn1 / 8;                // 16-byte chunks per row
       for (int i = tid; i < nrow * kCpr; i += kThreads) {
@@ -581,7 +581,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
         st16c(rh, (uint32_t)((pos0 + row) * m.I + n * bn1 + 8 * ch) * 2u,
               *reinterpret_cast<const i32x4*>(hl + row * kHs + 8 * ch));
       }
-      __syncthreads();   // the ring slot is refilled by the next task
+      lds_barrier();     // the ring slot is refilled by the next task; the stores stay in flight
     } else {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -670,7 +670,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
               for (int r = 0; r < 4; ++r)
                 yl[(16 * mm + 4 * (lane >> 4) + r) * kYs + cw + 16 * j + (lane & 15)] =
                     tile.acc[2 * q + mm][j][r];
-          __syncthreads();
+          lds_barrier();
           const int nr = min(32, nrow - 32 * q);
           constexpr int kCpr = bn2 / 4;            // 16-byte chunks per row
           for (int i = tid; i < nr * kCpr; i += kThreads) {
@@ -678,7 +678,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
             st16c(ry, (uint32_t)((pos0 + 32 * q + row) * m.H + n2 * bn2 + 4 * ch) * 4u,
                   *reinterpret_cast<const i32x4*>(yl + row * kYs + 4 * ch));
           }
-          __syncthreads();
+          lds_barrier();   // the stores stay in flight
         }
     } else {
 #pragma unroll
