@@ -148,12 +148,23 @@ struct StreamTile {
   }
 };
 
-#define ET_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-
 // 16 bytes per lane, global -> LDS at lds_base + 16 * lane (sc1 when COH).
+// Issued from inline asm: the compiler's own wait insertion cannot tell the
+// ring slots' copies apart and would drain every copy in flight before each
+// LDS read; the tiles order the copies themselves with explicit vmcnt waits
+// and barriers.  M0 (the LDS base of the copy) is restored afterwards.
 template <bool COH>
 __device__ __forceinline__ void dma16(Rsrc r, void* lds_base, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ET_LDS_PTR(lds_base), 16, voff, 0, 0, COH ? 16 : 0);
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  uint32_t save;
+  if constexpr (COH)
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen sc1 lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(save) : "s"(l), "v"(voff), "s"(r) : "memory");
+  else
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(save) : "s"(l), "v"(voff), "s"(r) : "memory");
 }
 
 // Workgroup barrier that waits for this wave's LDS accesses only (the
@@ -181,116 +192,190 @@ struct RingTile {
 
   f32x4 acc[MT][4];
 
+  // fragment i of a K-step (i < 4: B group i of this wave, else A group i-4)
+  __device__ static __forceinline__ i32x4 frag(const unsigned char* slot, uint32_t fo, int wave, int i) {
+    const unsigned char* p = i < 4 ? slot + kRows * 128 + wave * 64 * 128 + i * 16 * 128
+                                   : slot + (i - 4) * 16 * 128;
+    return *reinterpret_cast<const i32x4*>(p + fo);
+  }
+
+  // One K-step over the valid 16-row groups (2 * NV of them): the MFMAs on
+  // (af, bf), two per group, fenced so that the next K-step's fragment reads
+  // (READ) and the copies dma(0..) of a later stage (DMA) sit between them.
+  // The next B fragments go to nbf; the next A fragments replace af[m] as
+  // soon as the MFMAs of row pair m have been issued.
+  template <int NV, bool READ, bool DMA, class DmaF>
+  __device__ __forceinline__ void kstep(i32x4* af, const i32x4* bf, const unsigned char* rslot,
+                                        uint32_t fo, int wave, i32x4* nbf, DmaF dma) {
+    constexpr int kNG = 4 * NV;                 // groups of two MFMAs
+    constexpr int kND = kLB + NV;               // copies (A copies of valid halves only)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < kNG; ++g) {
+      const int m = 2 * (g / 4), n = g % 4;
+      acc[m][n] = mfma16(af[m], bf[n], acc[m][n]);
+      acc[m + 1][n] = mfma16(af[m + 1], bf[n], acc[m + 1][n]);
+      if constexpr (READ) {
+        if (g < 4) nbf[g] = frag(rslot, fo, wave, g);
+        if (n == 3) {
+          af[m] = frag(rslot, fo, wave, 4 + m);
+          af[m + 1] = frag(rslot, fo, wave, 5 + m);
+        }
+      }
+      if constexpr (DMA) {
+#pragma unroll
+        for (int i = g * kND / kNG; i < (g + 1) * kND / kNG; ++i) dma(i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
   // rb[n] / b_row0[n]: buffer and byte offset of the first row (output
   // column) of this wave's 16-column group n; rows are b_stride bytes apart.
-  // s0, s1, s2: the three ring slots, three distinct __shared__ arrays of
-  // kStageBytes each -- distinct objects let the compiler wait only for the
-  // copies into the slot being read, so two stages stay in flight.
-  // mv: 16-row groups holding valid rows (1..MT); the MFMAs of the others
-  // are skipped (their rows read as zeros and their results are not stored).
+  // s0, s1, s2: the three ring slots, kStageBytes each.
+  // mv: 16-row groups holding valid rows (1..MT); 32-row halves beyond them
+  // are neither copied nor multiplied (their rows would read as zeros and
+  // their results are not stored).
   template <class Gate>
   __device__ __forceinline__ bool run(Rsrc ra, const uint32_t* a_row_off /* [kRows], LDS */,
                                       const Rsrc* rb, const uint32_t* b_row0, uint32_t b_stride,
                                       int K, Gate gate, unsigned char* s0, unsigned char* s1,
                                       unsigned char* s2, int mv = MT) {
+    const int nv = (min(max(mv, 1), MT) + 1) >> 1;    // valid 32-row halves
+    if constexpr (MT >= 8) {
+      if (nv == 4) return body<4>(ra, a_row_off, rb, b_row0, b_stride, K, gate, s0, s1, s2);
+      if (nv == 3) return body<3>(ra, a_row_off, rb, b_row0, b_stride, K, gate, s0, s1, s2);
+    }
+    if constexpr (MT >= 4)
+      if (nv == 2) return body<2>(ra, a_row_off, rb, b_row0, b_stride, K, gate, s0, s1, s2);
+    return body<1>(ra, a_row_off, rb, b_row0, b_stride, K, gate, s0, s1, s2);
+  }
+
+  // Software pipeline over 64-element K-stages held in a ring of three LDS
+  // slots, all three in flight ahead of the MFMAs.  Per stage ks (slot cur):
+  // K-step 0 multiplies fragments already in VGPRs while reading K-step 1's;
+  // then the wait for stage ks+1 (this wave's copies, then the barrier for
+  // everyone's -- which also tells that every wave is done reading slot cur);
+  // K-step 1 multiplies while stage ks+1's first fragments are read and
+  // stage ks+3 is copied into slot cur.
+  template <int NV, class Gate>
+  __device__ __forceinline__ bool body(Rsrc ra, const uint32_t* a_row_off, const Rsrc* rb,
+                                       const uint32_t* b_row0, uint32_t b_stride, int K, Gate gate,
+                                       unsigned char* s0, unsigned char* s1, unsigned char* s2) {
+    constexpr int kLAv = NV;                    // A copies per wave per stage (valid halves)
+    constexpr int kLv = kLB + kLAv;
+    constexpr int kNR = 4 + 2 * NV;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nks = K / 64;
-    const int crow = lane >> 3, cpos = lane & 7;           // this lane's row / chunk in a copy
+    const int crow = lane >> 3, cpos = lane & 7;   // this lane's row / chunk in a copy
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // B copies: wave-local rows 8q + crow (group q / 2); logical chunk of this
-    // lane's physical slot cpos is cpos ^ ((row / 2) mod 8)
+    // B copies: wave-local rows 8q + crow (group q / 2); the logical chunk of
+    // this lane's physical slot cpos is cpos ^ ((row / 2) mod 8)
     uint32_t boff[kLB];
 #pragma unroll
     for (int q = 0; q < kLB; ++q) {
-      const int j = 8 * (q & 1) + crow;                    // row inside group q / 2
+      const int j = 8 * (q & 1) + crow;
       const int c = cpos ^ ((j >> 1) & 7);
       boff[q] = b_row0[q >> 1] + (uint32_t)j * b_stride + 16u * c;
     }
-    auto issue_b = [&](int ks, unsigned char* slot) {
-      unsigned char* dst = slot + kRows * 128 + wave * 64 * 128;
-#pragma unroll
-      for (int q = 0; q < kLB; ++q) dma16<false>(rb[q >> 1], dst + q * 1024, boff[q] + ks * 128u);
-    };
-    uint32_t aoff[kLA];
-    auto issue_a = [&](int ks, unsigned char* slot) {
-#pragma unroll
-      for (int u = 0; u < kLA; ++u) dma16<COH>(ra, slot + (wave + 4 * u) * 1024, aoff[u] + ks * 128u);
+    uint32_t aoff[kLAv];
+    // copy i of stage ks into slot: i < kLB weight rows, else A half i - kLB
+    auto dma_one = [&](int i, int ks, unsigned char* slot) ET_INLINE {
+      if (i < kLB)
+        dma16<false>(rb[i >> 1], slot + kRows * 128 + wave * 64 * 128 + i * 1024, boff[i] + ks * 128u);
+      else
+        dma16<COH>(ra, slot + (wave + 4 * (i - kLB)) * 1024, aoff[i - kLB] + ks * 128u);
     };
 
-    issue_b(0, s0);
-    if (nks > 1) issue_b(1, s1);
+    // the weights of the first stages are requested before the gate
+#pragma unroll
+    for (int q = 0; q < kLB; ++q) dma_one(q, 0, s0);
+    if (nks > 1)
+#pragma unroll
+      for (int q = 0; q < kLB; ++q) dma_one(q, 1, s1);
+    if (nks > 2)
+#pragma unroll
+      for (int q = 0; q < kLB; ++q) dma_one(q, 2, s2);
     if (!gate(0)) {
       wait_vm_barrier<0>();
       return false;
     }
 #pragma unroll
-    for (int u = 0; u < kLA; ++u) {
+    for (int u = 0; u < kLAv; ++u) {
       const int row = 8 * (wave + 4 * u) + crow;
       const uint32_t base = a_row_off[row];
       aoff[u] = base == kOOB ? kOOB : base + 16u * (uint32_t)(cpos ^ ((row >> 1) & 7));
     }
-    issue_a(0, s0);
-    if (nks > 1) issue_a(1, s1);
+#pragma unroll
+    for (int u = 0; u < kLAv; ++u) dma_one(kLB + u, 0, s0);
+    if (nks > 1)
+#pragma unroll
+      for (int u = 0; u < kLAv; ++u) dma_one(kLB + u, 1, s1);
+    if (nks > 2)
+#pragma unroll
+      for (int u = 0; u < kLAv; ++u) dma_one(kLB + u, 2, s2);
 
     // fragment read offsets: row (lane % 16) of each 16-row group, logical
-    // chunk 4s + g -> physical chunk (4s + g) ^ ((lane % 16) / 2 mod 8)
+    // chunk 4h + g -> physical chunk (4h + g) ^ ((lane % 16) / 2 mod 8)
     const int fi = lane & 15, fg = lane >> 4;
     uint32_t foff[2];
 #pragma unroll
-    for (int s2i = 0; s2i < 2; ++s2i)
-      foff[s2i] = (uint32_t)fi * 128u + 16u * (uint32_t)((4 * s2i + fg) ^ ((fi >> 1) & 7));
+    for (int h = 0; h < 2; ++h)
+      foff[h] = (uint32_t)fi * 128u + 16u * (uint32_t)((4 * h + fg) ^ ((fi >> 1) & 7));
 
-    // one stage: wait for slot `cur` (this wave's copies, then the barrier for
-    // everyone's), refill slot `nxt2` (read two stages ago) with stage ks + 2,
-    // then the MFMAs of stage ks
-    auto step = [&](int ks, const unsigned char* cur, unsigned char* nxt2) {
-      if (ks >= nks) return;
-      if (ks == 0 || ks + 1 >= nks)
-        wait_vm_barrier<0>();
-      else
-        wait_vm_barrier<kL>();      // stage ks + 1 may still be in flight
-      if (ks + 2 < nks) {
-        issue_b(ks + 2, nxt2);
-        issue_a(ks + 2, nxt2);
-      }
-      const unsigned char* sb = cur + kRows * 128 + wave * 64 * 128;
-      // each 32-element K-step reads all of its fragments first, then runs
-      // its MFMAs (the LDS latency is paid once per K-step); 32-row halves
-      // beyond the valid rows are skipped
+    // stage 0 complete: only the A copies of stages 1 and 2 were issued after it
+    if (nks > 2) wait_vm_barrier<2 * kLAv>();
+    else if (nks > 1) wait_vm_barrier<kLAv>();
+    else wait_vm_barrier<0>();
+    i32x4 fa[MT], fb0[4], fb1[4];
 #pragma unroll
-      for (int s2i = 0; s2i < 2; ++s2i) {
-        i32x4 bf[4], af[MT];
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-          bf[n] = *reinterpret_cast<const i32x4*>(sb + n * 16 * 128 + foff[s2i]);
-#pragma unroll
-        for (int m = 0; m < MT; m += 2)
-          if (m < mv) {
-            af[m] = *reinterpret_cast<const i32x4*>(cur + m * 16 * 128 + foff[s2i]);
-            af[m + 1] = *reinterpret_cast<const i32x4*>(cur + (m + 1) * 16 * 128 + foff[s2i]);
-          }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int m = 0; m < MT; m += 2)
-          if (m < mv) {
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-              acc[m][n] = mfma16(af[m], bf[n], acc[m][n]);
-              acc[m + 1][n] = mfma16(af[m + 1], bf[n], acc[m + 1][n]);
-            }
-          }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int i = 0; i < kNR; ++i) {
+      if (i < 4) fb0[i] = frag(s0, foff[0], wave, i);
+      else fa[i - 4] = frag(s0, foff[0], wave, i);
+    }
+    auto no_dma = [](int) {};
+    // slot of stage ks: ring position ks mod 3 (rotated at run time, so the
+    // steady-state stage is one copy of code)
+    unsigned char* cur = s0;
+    unsigned char* nxt = s1;
+    unsigned char* nx2 = s2;
+    auto rotate = [&]() ET_INLINE {
+      unsigned char* t = cur;
+      cur = nxt;
+      nxt = nx2;
+      nx2 = t;
     };
-    for (int ks = 0; ks < nks; ks += 3) {
-      step(ks, s0, s2);
-      step(ks + 1, s1, s0);
-      step(ks + 2, s2, s1);
+    // stage 1's wait: after it only stage 2's A copies were issued; later
+    // stages wait with stage ks+2 (all of its copies) still in flight
+    auto wait_next = [&](int ks) ET_INLINE {
+      if (ks == 0) wait_vm_barrier<kLAv>();
+      else wait_vm_barrier<kLv>();
+    };
+    int ks = 0;
+    for (; ks + 3 < nks; ++ks) {            // steady state: stage ks+3 is copied into slot cur
+      kstep<NV, true, false>(fa, fb0, cur, foff[1], wave, fb1, no_dma);
+      wait_next(ks);
+      unsigned char* dst = cur;
+      const int kd = ks + 3;
+      kstep<NV, true, true>(fa, fb1, nxt, foff[0], wave, fb0,
+                            [&](int i) ET_INLINE { dma_one(i, kd, dst); });
+      rotate();
+    }
+    for (; ks < nks; ++ks) {                // the last (up to) three stages
+      kstep<NV, true, false>(fa, fb0, cur, foff[1], wave, fb1, no_dma);
+      if (ks + 1 < nks) {
+        if (ks + 2 < nks) wait_next(ks);
+        else wait_vm_barrier<0>();
+        kstep<NV, true, false>(fa, fb1, nxt, foff[0], wave, fb0, no_dma);
+      } else {
+        kstep<NV, false, false>(fa, fb1, nxt, foff[0], wave, fb0, no_dma);
+      }
+      rotate();
     }
     wait_vm_barrier<0>();            // the ring may be refilled by the next task
     return true;
