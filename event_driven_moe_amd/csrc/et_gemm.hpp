@@ -55,7 +55,7 @@ struct StreamTile {
                                       const Rsrc* rb, const uint32_t* b_row_off /* [NB] */,
                                       int nkb, Gate gate, float* red /* LDS kRedFloats */) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar registers
     const int wk = wave % WK;
     const uint32_t kg = (uint32_t)(lane >> 4) * 64u;
     uint32_t aoff[MT];
@@ -266,7 +266,7 @@ struct RingTile {
     constexpr int kLv = kLB + kLAv;
     constexpr int kNR = 4 + 2 * NV;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar registers
     const int nks = K / 64;
     const int crow = lane >> 3, cpos = lane & 7;   // this lane's row / chunk in a copy
 #pragma unroll

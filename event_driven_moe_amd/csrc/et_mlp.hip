@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kThreads, kMlpOcc<MT>) void mlp_kernel(RunArgs ra, 
   const int n_gate = mb * ngt;
   const int n_down = mb * ndt;
   const int total = n_gate + n_down;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   auto set_rows = [&](int b, int row_bytes) ET_INLINE {
     for (int i = threadIdx.x; i < rows; i += kThreads) {

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   Ctx c;
   if (!prologue(c, ra, &sh)) return;
   const int sched = ra.sched;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar registers
   const int rows = 16 * MT;
   const int nt1 = m.I / bn1, nt2 = m.H / bn2;
   const int NR = m.NR;
@@ -971,17 +971,18 @@ int launch_moe(const LaunchCommon& lc, const float* logits, const uint16_t* x, i
   ra.n_single = 2 * m.NR + 1;   // routing and grouping: one slot per claim
   ra.total_hint = kUnknownTotal;
   ra.extent = mp.extent(T, tl);
-  const void* const kernels[TV_COUNT] = {
+  const void* const kernels[] = {
       reinterpret_cast<const void*>(&moe_kernel<TV_M16>),
       reinterpret_cast<const void*>(&moe_kernel<TV_M32>),
       reinterpret_cast<const void*>(&moe_kernel<TV_M64>),
       reinterpret_cast<const void*>(&moe_kernel<TV_W64>),
       reinterpret_cast<const void*>(&moe_kernel<TV_W128>),
       reinterpret_cast<const void*>(&moe_kernel<TV_M16W>)};
+  static_assert(sizeof(kernels) / sizeof(kernels[0]) == TV_COUNT, "one kernel per tile variant");
   const void* k = kernels[tv];
-  constexpr int occ[TV_COUNT] = {MoeCfg<TV_M16>::kOcc, MoeCfg<TV_M32>::kOcc, MoeCfg<TV_M64>::kOcc,
-                                 MoeCfg<TV_W64>::kOcc, MoeCfg<TV_W128>::kOcc,
-                                 MoeCfg<TV_M16W>::kOcc};
+  constexpr int occ[] = {MoeCfg<TV_M16>::kOcc, MoeCfg<TV_M32>::kOcc, MoeCfg<TV_M64>::kOcc,
+                         MoeCfg<TV_W64>::kOcc, MoeCfg<TV_W128>::kOcc, MoeCfg<TV_M16W>::kOcc};
+  static_assert(sizeof(occ) / sizeof(occ[0]) == TV_COUNT, "one occupancy per tile variant");
   LaunchCommon l = lc;
   l.G = lc.G * occ[tv];
   if (lc.sched == ET_SCHED_PER_OP) {
