@@ -88,8 +88,9 @@ struct RunArgs {
 // Workgroup-shared scratch for broadcasts and keyed pushes.
 struct Shared {
   int v[8];
-  int qn[kMaxShards];     // push: tasks per shard, then running rank
+  int qn[kMaxShards];     // push: tasks per shard, then slots filled so far
   int qb[kMaxShards];     // push: first slot per shard
+  int wq[kThreads / 64][kMaxShards];   // push: items per wave and shard in a round
 };
 
 struct Ctx {
@@ -248,13 +249,14 @@ __device__ __forceinline__ int* q_pushed(const RunArgs& a, int q) {
 // tile) are claimed by workers of one XCD and share its L2.  Whole
 // workgroup; must follow wg_release() (or a fired wg_notify) so the pushed
 // tasks' inputs are complete before their slots are published.  One atomic
-// per shard reserves the slots, then each slot is written; a claimer that
-// finds a reserved slot still empty waits for the write.
+// per shard reserves the slots, then each slot is written, each shard's in
+// push order; a claimer that finds a reserved slot still empty waits for the
+// write.
 template <class F, class K>
 __device__ __forceinline__ void wg_push(const Ctx& c, int n, F id_of, K key_of) {
   if (n <= 0) return;
   const int nq = c.a.nq;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid < kMaxShards) c.sh->qn[tid] = 0;
   __syncthreads();
   if (nq > 1)
@@ -268,15 +270,37 @@ __device__ __forceinline__ void wg_push(const Ctx& c, int n, F id_of, K key_of) 
     c.sh->qn[tid] = 0;
   }
   __syncthreads();
-  for (int i = tid; i < n; i += kThreads) {
-    const int q = nq > 1 ? (key_of(i) & (kMaxShards - 1)) : 0;
-    const int s = c.sh->qb[q] + atomicAdd(&c.sh->qn[q], 1);
-    if (s < c.a.q_cap)
-      st_rlx(&c.a.slots[(size_t)q * c.a.q_cap + s], id_of(i) + 1);
-    else
-      raise_fault(c.a, ET_ESTATE, -1, s, c.a.q_cap);
+  // Slots in push order: item i takes its shard's next slot in index order
+  // (rank among the round's earlier items of the same shard: a ballot per
+  // shard within the wave, plus the counts of the waves before it).
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  for (int i0 = 0; i0 < n; i0 += kThreads) {
+    const int i = i0 + tid;
+    const int q = i < n ? (nq > 1 ? (key_of(i) & (kMaxShards - 1)) : 0) : -1;
+    int rank = 0;
+    for (int sq = 0; sq < nq; ++sq) {
+      const uint64_t m = __ballot(q == sq);
+      if (q == sq) rank = __popcll(m & below);
+      if (lane == 0) c.sh->wq[wave][sq] = __popcll(m);
+    }
+    __syncthreads();
+    if (q >= 0) {
+      int off = c.sh->qn[q] + rank;
+      for (int w = 0; w < wave; ++w) off += c.sh->wq[w][q];
+      const int sl = c.sh->qb[q] + off;
+      if (sl < c.a.q_cap)
+        st_rlx(&c.a.slots[(size_t)q * c.a.q_cap + sl], id_of(i) + 1);
+      else
+        raise_fault(c.a, ET_ESTATE, -1, sl, c.a.q_cap);
+    }
+    __syncthreads();
+    if (tid < nq) {
+      int t = 0;
+      for (int w = 0; w < kThreads / 64; ++w) t += c.sh->wq[w][tid];
+      c.sh->qn[tid] += t;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 }
 
 // Set the total number of tasks of this call (dynamic mode), once known.

@@ -65,7 +65,7 @@ struct MoeArgs {
   float* y;
   int T, H, I, E, k, NR, tpr;
   int ccols;           // combine tile columns
-  int ev_exp, ev_h, ev_c;
+  int ev_exp, ev_he, ev_h, ev_c;
 };
 
 // LDS: three slot arrays (the GEMM ring of the wide variants; scratch for
@@ -604,12 +604,18 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       t0_notify(c, EV_G1ALL, 1, meta(MD_TOTAL1), task);
     } else if (sched == ET_SCHED_STATIC) {
       t0_notify(c, m.ev_h + gb, 1, nt1, task);
-    } else if (wg_notify(c, m.ev_h + gb, 1, nt1, task)) {
-      // block gb's down tasks: expert e's range, one per column tile
+    } else {
+      // dynamic: the expert's event counts its gate/up tiles over all of its
+      // blocks (a data-dependent wait count); the notify that completes it
+      // pushes all of the expert's down tasks, in (column tile, block) order,
+      // so the blocks sharing a weight tile are claimed together from one
+      // shard and stream that tile through the XCD's L2 once
       const int nblk = c_blk[e + 1] - c_blk[e];
-      const int b2 = base1 + meta(MD_TOTAL1) + c_blk[e] * nt2 + (gb - c_blk[e]);
-      wg_push(c, nt2, [&](int i) { return b2 + i * nblk; },
-              [&](int i) { return e * nt2 + i; });   // key: the weight tile (e, column tile)
+      if (wg_notify(c, m.ev_he + e, 1, nblk * nt1, task)) {
+        const int b2 = base1 + meta(MD_TOTAL1) + c_blk[e] * nt2;
+        wg_push(c, nblk * nt2, [&](int i) { return b2 + i; },
+                [&](int i) { return e * nt2 + i / nblk; });   // key: the weight tile (e, column tile)
+      }
     }
     return true;
   };
@@ -964,6 +970,7 @@ int launch_moe(const LaunchCommon& lc, const float* logits, const uint16_t* x, i
   // workgroups without a tile
   m.ccols = cdiv(T, kCombTok) * cdiv(m.H, kCombCols) >= lc.G ? kCombCols : kCombColsMin;
   m.ev_exp = mp.ev_exp();
+  m.ev_he = mp.ev_he();
   m.ev_h = mp.ev_h();
   m.ev_c = mp.ev_c();
   RunArgs ra = lc.run_args();

@@ -121,7 +121,8 @@ struct MlpPlan {
 //   EV_G1ALL  all gate/up tasks done      (total1)        [barrier mode]
 //   EV_DOWN   all down tasks done         (total2)        [barrier]
 //   EV_EXP[e] rows of expert e grouped    (counts[e])     data-dependent
-//   EV_H[gb]  gate/up tiles of block gb   (inter / bn1)
+//   EV_HE[e]  gate/up tiles of expert e   (blocks[e] * inter / bn1) data-dependent [dynamic]
+//   EV_H[gb]  gate/up tiles of block gb   (inter / bn1)                    [static]
 //   EV_C[t][c] down tiles covering token t, column tile c (top_k) [static, dynamic]
 // tasks: [0, R) routing, R scan, [R+1, 2R+1) grouping, then total1 gate/up
 //   tiles (block-major, column tile fastest), total2 down tiles, then (barrier,
@@ -145,7 +146,8 @@ struct MoePlan {
   int t_max, hidden, inter, n_experts, top_k, n_route;
   ET_HD int nb_max() const { return cdiv(t_max * top_k, kMinRows) + n_experts; }
   ET_HD int ev_exp() const { return EV_FIXED; }
-  ET_HD int ev_h() const { return EV_FIXED + n_experts; }
+  ET_HD int ev_he() const { return EV_FIXED + n_experts; }
+  ET_HD int ev_h() const { return EV_FIXED + 2 * n_experts; }
   ET_HD int ev_c() const { return ev_h() + nb_max(); }
   ET_HD int n_events_max() const { return ev_c() + t_max * (hidden / kMinCols); }
   ET_HD int extent(int T, const Tiling& t) const { return ev_c() + T * (hidden / t.bn2); }

@@ -82,7 +82,9 @@ def moe_table(counts, rows_per_tile, inter, gate_cols, hidden, down_cols, n_rout
     ``n_route`` grouping tasks; expert e owns ceil(counts[e]/rows) row blocks;
     each block has inter/gate_cols gate/up tiles and hidden/down_cols down
     tiles.  E_exp[e] starts at counts[e] (data-dependent); E_h[block] at the
-    number of gate/up tiles of a block."""
+    number of gate/up tiles of a block; E_he[e] (the dynamic schedule's
+    per-expert edge from gate/up to down tiles) at the number of gate/up
+    tiles over all of expert e's blocks (data-dependent)."""
     counts = np.asarray(counts, dtype=np.int64)
     blocks = -(-counts // rows_per_tile)
     nb = int(blocks.sum())
@@ -97,6 +99,8 @@ def moe_table(counts, rows_per_tile, inter, gate_cols, hidden, down_cols, n_rout
             "E_exp": {"shape": (counts.shape[0],), "wait_count": counts.copy()},
             "E_h": {"shape": (nb,),
                     "wait_count": np.full(nb, inter // gate_cols, np.int64)},
+            "E_he": {"shape": (counts.shape[0],),
+                     "wait_count": blocks * (inter // gate_cols)},
         },
     }
 

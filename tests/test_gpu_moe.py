@@ -101,8 +101,9 @@ def test_fetch_batches(fetch):
 @pytest.mark.parametrize("sched", ["static", "dynamic"])
 def test_event_invariants(sched, T):
     """Each task ran once; the data-dependent expert events ended at their
-    run-time wait counts (rows routed to each expert), block events at the
-    number of gate/up tiles of a block."""
+    run-time wait counts (rows routed to each expert; dynamic: also the
+    gate/up tiles over each expert's blocks), the static schedule's block
+    events at the number of gate/up tiles of a block."""
     name = "moe_skewed"
     ws = _ws(name, 1024)
     ws.runs().zero_()
@@ -119,13 +120,17 @@ def test_event_invariants(sched, T):
     assert (runs[:total] == 1).all() and (runs[total:] == 0).all()
     cnt = ws.counters(1 - st["bank"]).cpu().numpy()
     assert cnt[0] == -nr                                   # all routing tasks notified
-    ev_exp, ev_h = 8, 8 + E
+    ev_exp, ev_he, ev_h = 8, 8 + E, 8 + 2 * E
     nb = tab["blocks"]
-    assert (cnt[ev_h:ev_h + nb] == -tab["events"]["E_h"]["wait_count"]).all()
     assert cnt[4] == -(nb * (H // bn2))                    # all down tiles done
     if sched == "dynamic":
+        # data-dependent: rows per expert, and gate/up tiles over its blocks
         assert (cnt[ev_exp:ev_exp + E] == -tab["events"]["E_exp"]["wait_count"]).all()
+        assert (cnt[ev_he:ev_he + E] == -tab["events"]["E_he"]["wait_count"]).all()
+        assert (cnt[ev_h:ev_h + nb] == 0).all()
     else:
+        assert (cnt[ev_h:ev_h + nb] == -tab["events"]["E_h"]["wait_count"]).all()
+        assert (cnt[ev_he:ev_he + E] == 0).all()
         assert cnt[1] == -1 and cnt[2] == -nr
     check_against_oracle(name, T, out, aux)
 

@@ -105,6 +105,10 @@ def test_task_indptr_brute_force():
         tab = events.moe_table(counts, bm, nt * 16, 16, 32, 32, 4)
         assert tab["tasks"]["gate_up"] == ip[-1]
         assert (tab["events"]["E_exp"]["wait_count"] == counts).all()
+        # E_he[e]: one notify per gate/up task of expert e (brute-force count)
+        he = events.notify_counts([(t, t[0]) for t in tasks], (len(counts),))
+        assert (tab["events"]["E_he"]["wait_count"] == he).all()
+        assert tab["events"]["E_he"]["wait_count"].sum() == tab["tasks"]["gate_up"]
 
 
 def _rand_experts(rng, E, H, I):
