@@ -612,9 +612,12 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       // shard and stream that tile through the XCD's L2 once
       const int nblk = c_blk[e + 1] - c_blk[e];
       if (wg_notify(c, m.ev_he + e, 1, nblk * nt1, task)) {
+        // block-major push order: a shard holds (block 0: its tiles), (block 1:
+        // its tiles), ..., so a batched claim mixes tiles of one block and the
+        // claims taken beside it stream the same tiles for the next blocks
         const int b2 = base1 + meta(MD_TOTAL1) + c_blk[e] * nt2;
-        wg_push(c, nblk * nt2, [&](int i) { return b2 + i; },
-                [&](int i) { return e * nt2 + i / nblk; });   // key: the weight tile (e, column tile)
+        wg_push(c, nblk * nt2, [&](int i) { return b2 + (i % nt2) * nblk + i / nt2; },
+                [&](int i) { return e * nt2 + i % nt2; });   // key: the weight tile (e, column tile)
       }
     }
     return true;
@@ -805,15 +808,24 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       // key of gate/up task i: its weight tile (expert, column tile); the
       // scan's block offsets per expert are still in LDS
       const int* blk = reinterpret_cast<const int*>(s1) + 1024;
-      wg_push(c, nb * nt1, [&](int i) { return base1 + i; }, [&](int i) {
+      auto expert_of = [&](int i) ET_INLINE {
         int lo = 0, hi = m.E;
         while (hi - lo > 1) {
           const int mid = (lo + hi) >> 1;
           if (blk[mid] * nt1 <= i) lo = mid; else hi = mid;
         }
-        const int nblk = (lo + 1 < m.E ? blk[lo + 1] : nb) - blk[lo];
-        return lo * nt1 + (i - blk[lo] * nt1) / nblk;
-      });
+        return lo;
+      };
+      wg_push(c, nb * nt1,
+              [&](int i) {   // block-major within the expert's range
+                const int e = expert_of(i), l = i - blk[e] * nt1;
+                const int nblk = (e + 1 < m.E ? blk[e + 1] : nb) - blk[e];
+                return base1 + blk[e] * nt1 + (l % nt1) * nblk + l / nt1;
+              },
+              [&](int i) {
+                const int e = expert_of(i);
+                return e * nt1 + (i - blk[e] * nt1) % nt1;
+              });
       return true;
     }
     if (task == NR) {   // the scan as a task of its own: barrier and per-op modes
@@ -857,8 +869,8 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
         const int e = fe[i];
         const int lo = ld_coh(&m.task_indptr[e]), hi = ld_coh(&m.task_indptr[e + 1]);
         const int nblk = (hi - lo) / nt1;
-        wg_push(c, hi - lo, [&](int j) { return base1 + lo + j; },
-                [&](int j) { return e * nt1 + j / nblk; });   // key: (expert, column tile)
+        wg_push(c, hi - lo, [&](int j) { return base1 + lo + (j % nt1) * nblk + j / nt1; },
+                [&](int j) { return e * nt1 + j % nt1; });   // key: (expert, column tile)
       }
       __syncthreads();
       return true;
