@@ -94,7 +94,7 @@ __device__ __forceinline__ int block_exscan(int* a, int n, int* tmp /* >= 8 ints
   }
   const int inc = wave_incl_scan(s);
   if (lane == 63) tmp[wave] = inc;
-  __syncthreads();
+  lds_barrier();
   int wbase = 0;
   for (int w = 0; w < wave; ++w) wbase += tmp[w];
   const int total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
@@ -105,7 +105,7 @@ __device__ __forceinline__ int block_exscan(int* a, int n, int* tmp /* >= 8 ints
     if (j < n) a[j] = run;
     run += v[i];
   }
-  __syncthreads();
+  lds_barrier();
   return total;
 }
 
@@ -179,6 +179,10 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   // static / dynamic with few routed pairs: grouping runs inline after the scan
   const bool inline_group = (sched == ET_SCHED_STATIC || sched == ET_SCHED_DYNAMIC) &&
                             m.T * m.k <= kInlinePairs;
+  // one routing chunk (static / dynamic): its workgroup runs the scan and the
+  // grouping right after it, so the histogram and the chosen experts stay in
+  // LDS and no global round trip or store-completion wait separates them
+  const bool solo_route = NR == 1 && inline_group;
   const int wc = m.k;   // EV_C wait count: the k rows of a token, one per down column tile
   const int ncomb = cdiv(m.T, kCombTok) * cdiv(m.H, m.ccols);   // combine tiles
 
@@ -286,6 +290,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   // -0.0 and +0.0 share a key), with two DPP reductions and no LDS traffic.
   auto route = [&](int r) ET_INLINE {
     int* hist_l = s_i;   // [E]
+    int* ids_l = reinterpret_cast<int*>(gen + kGenIdx);   // [T * k] when solo_route
     for (int e = tid; e < m.E; e += kThreads) hist_l[e] = 0;
     __syncthreads();
     const int t0 = r * m.tpr;
@@ -356,6 +361,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
             st_coh(&m.topk_ids[t * m.k + lane], my_e[b]);
             st_coh(&m.topk_w[t * m.k + lane], ex / sum);
             atomicAdd(&hist_l[my_e[b]], 1);
+            if (solo_route) ids_l[t * m.k + lane] = my_e[b];
           }
         }
       }
@@ -365,8 +371,9 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     else if (m.E <= 128) route_tokens(integral_constant<int, 2>{}, integral_constant<int, 4>{});
     else if (m.E <= 256) route_tokens(integral_constant<int, 4>{}, integral_constant<int, 2>{});
     else route_tokens(integral_constant<int, kMaxExperts / 64>{}, integral_constant<int, 1>{});
-    __syncthreads();
-    for (int e = tid; e < m.E; e += kThreads) st_coh(&m.hist[r * m.E + e], hist_l[e]);
+    lds_barrier();   // the histogram is complete; the id and weight stores stay in flight
+    if (!solo_route)
+      for (int e = tid; e < m.E; e += kThreads) st_coh(&m.hist[r * m.E + e], hist_l[e]);
   };
 
   // ------------------------------------------------------------- scan
@@ -378,8 +385,9 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     int* part = tmp + 8;                   // [256] chunk sums
     const int n_ne = cdiv(m.T, m.tpr);
     const int tot = n_ne * m.E;
-    // all histogram loads in flight at once (16 per thread per pass)
-    for (int b0 = 0; b0 < tot; b0 += 16 * kThreads) {
+    // all histogram loads in flight at once (16 per thread per pass); a solo
+    // routing chunk left its histogram in hs already
+    for (int b0 = 0; !solo_route && b0 < tot; b0 += 16 * kThreads) {
       int v[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
@@ -421,7 +429,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
         st_coh(&m.counts[e], run);
       }
     }
-    __syncthreads();
+    lds_barrier();
     block_exscan(cnt, m.E, tmp);           // cnt -> tok_indptr
     const int nb = block_exscan(blk, m.E, tmp);
     for (int e = tid; e < m.E; e += kThreads) {
@@ -440,7 +448,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       st_rlx(&ra.hdr[HDR_META + MD_TOTAL1], nb * nt1);
       st_rlx(&ra.hdr[HDR_META + MD_TOTAL2], nb * nt2);
     }
-    __syncthreads();
+    lds_barrier();   // every caller releases (store-completion wait) before notifying
     return nb;
   };
 
@@ -486,8 +494,9 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     int* ids = reinterpret_cast<int*>(gen + kGenIdx);   // [T * k] (the index cache is not yet in use)
     cached = false;
     const int np = m.T * m.k;
-    for (int q = tid; q < np; q += kThreads) ids[q] = ld_coh(&m.topk_ids[q]);
-    __syncthreads();
+    if (!solo_route)   // a solo routing chunk left the chosen experts here already
+      for (int q = tid; q < np; q += kThreads) ids[q] = ld_coh(&m.topk_ids[q]);
+    lds_barrier();
     const int n_ne = cdiv(m.T, m.tpr);
     for (int r = wave; r < n_ne; r += 4) {
       const int t1 = min(m.T, (r + 1) * m.tpr);
@@ -501,7 +510,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
         }
       }
     }
-    __syncthreads();
+    lds_barrier();   // the caller releases before notifying
   };
 
   // ------------------------------------------------------------- gemm tiles
@@ -756,12 +765,17 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     if (task < NR) {
       route(task);
       if (sched == ET_SCHED_PER_OP) return true;
-      wg_release();
-      if (sched == ET_SCHED_BARRIER) {
+      if (solo_route) {
+        // EV_ROUTE's only consumer is this workgroup's scan, which reads LDS
         t0_notify(c, EV_ROUTE, 1, NR, task);
-        return true;
+      } else {
+        wg_release();
+        if (sched == ET_SCHED_BARRIER) {
+          t0_notify(c, EV_ROUTE, 1, NR, task);
+          return true;
+        }
+        if (!wg_notify(c, EV_ROUTE, 1, NR, task)) return true;
       }
-      if (!wg_notify(c, EV_ROUTE, 1, NR, task)) return true;
       // this notify completed EV_ROUTE: the scan runs here
       long long ts = trace_now(c);
       const int nb = scan();
