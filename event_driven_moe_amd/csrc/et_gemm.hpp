@@ -3,12 +3,14 @@
 // Both tiles accumulate in fp32 with v_mfma_f32_16x16x32_bf16 and take the
 // weights (B) K-contiguous ([N, K]) straight from global memory into VGPRs in
 // MFMA operand layout: lane (j = lane%16, g = lane/16) of a 16-column group
-// holds column j.  For one 128-element K-block, lane group g loads the 64
-// contiguous bytes [64g, 64g + 64) of its row as four 16-byte loads, so four
-// lanes cover 256 contiguous bytes of a weight row: whole cache lines of the
-// weight stream.  MFMA step s (0..3) consumes elements 32g + 8s .. 32g + 8s + 7
-// of both operands; the reduction runs over all 128 elements, so this K
-// permutation is harmless as long as A uses the same one.
+// holds column j.  For one 128-element K-block, the s-th of four 16-byte
+// loads takes chunk 4s + g of the row's 256 bytes, so one load instruction
+// covers 64 contiguous bytes of each of its 16 rows (16 memory sectors for
+// 1 KB; with the chunks of a lane group adjacent instead, one instruction
+// touched 64 sectors and the streaming rate per CU was a quarter as high),
+// and the four loads together read whole cache lines of the weight stream.
+// MFMA step s (0..3) consumes elements 32s + 8g .. 32s + 8g + 7 of both
+// operands, the MFMA's natural K order.
 //
 // StreamTile (few rows, the decode regime): A also streams from global memory
 // into VGPRs (lane (i = lane%16, g) holds row i).  The four waves split the
@@ -57,7 +59,7 @@ struct StreamTile {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar registers
     const int wk = wave % WK;
-    const uint32_t kg = (uint32_t)(lane >> 4) * 64u;
+    const uint32_t kg = (uint32_t)(lane >> 4) * 16u;   // chunk 4 s + g of a K-block row
     uint32_t aoff[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -75,7 +77,7 @@ struct StreamTile {
 #pragma unroll
         for (int n = 0; n < NB; ++n)
 #pragma unroll
-          for (int s = 0; s < 4; ++s) bbuf[p][n][s] = ld16(rb[n], b_row_off[n] + o + 16u * s);
+          for (int s = 0; s < 4; ++s) bbuf[p][n][s] = ld16(rb[n], b_row_off[n] + o + 64u * s);
       }
     };
     auto load_a = [&](int p, int round) {
@@ -85,7 +87,7 @@ struct StreamTile {
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
-          for (int s = 0; s < 4; ++s) abuf[p][m][s] = ld16x<COH>(ra, aoff[m] + o + 16u * s);
+          for (int s = 0; s < 4; ++s) abuf[p][m][s] = ld16x<COH>(ra, aoff[m] + o + 64u * s);
       }
     };
 
