@@ -73,9 +73,14 @@ struct MoeArgs {
 constexpr int kScanHistBytes = kHistEntries * 4;                    // slot 0
 constexpr int kScanTempBytes = (2 * kMaxExperts + 8 + kThreads) * 4; // slot 1
 constexpr int kGenRowsOff = 0, kGenFired = 512, kGenIdx = 1024;
-// dynamic mode: combine inline in the down tile completing a token's rows
-// (EV_C), or as tiles pushed when the last down tile finishes (EV_DOWN)
-constexpr bool kInlineCombine = false;
+// Static and dynamic schedules with at most this many tokens: the combine
+// runs inline in the down tile whose notify completes a token's k rows for
+// its column tile (EV_C), instead of as tiles after the last down tile
+// (EV_DOWN).  It saves the wait for every down tile at T = 1 (static 33.2 ->
+// 32.4 us, dynamic 47.0 -> 42.6 us); from 8 tokens on the per-row notifies
+// cost as much as they save, and at 64 tokens (64-row blocks) far more
+// (moe_skewed T=64 static 94 -> 115 us).
+constexpr int kInlineCombineTokens = 4;
 constexpr int kIdxCache = 2 * (kMaxExperts + 1) * 4;   // tok_indptr + blk_indptr copies
 constexpr int kGenBytes = kGenIdx + kIdxCache;
 
@@ -184,7 +189,9 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   // LDS and no global round trip or store-completion wait separates them
   const bool solo_route = NR == 1 && inline_group;
   const int wc = m.k;   // EV_C wait count: the k rows of a token, one per down column tile
-  const int ncomb = cdiv(m.T, kCombTok) * cdiv(m.H, m.ccols);   // combine tiles
+  const bool inline_comb = (sched == ET_SCHED_STATIC || sched == ET_SCHED_DYNAMIC) &&
+                           m.T <= kInlineCombineTokens;
+  const int ncomb = inline_comb ? 0 : cdiv(m.T, kCombTok) * cdiv(m.H, m.ccols);   // combine tiles
 
   // LDS carve-outs (task kinds never overlap in time inside one workgroup)
   int* s_i = reinterpret_cast<int*>(s0);                              // route / scan / group
@@ -713,7 +720,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     }
     if (sched == ET_SCHED_PER_OP) return true;
     wg_release();
-    if (sched != ET_SCHED_DYNAMIC || !kInlineCombine) {
+    if (!inline_comb) {
       if (sched != ET_SCHED_DYNAMIC) {
         t0_notify(c, EV_DOWN, 1, meta(MD_TOTAL2), task);
       } else if (wg_notify(c, EV_DOWN, 1, meta(MD_TOTAL2), task)) {
@@ -783,7 +790,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       trace_task(c, NR, ts);
       if (!inline_group) {
         if (sched == ET_SCHED_DYNAMIC) {
-          set_total(c, 2 * NR + nb * (nt1 + nt2) + (kInlineCombine ? 0 : ncomb));
+          set_total(c, 2 * NR + nb * (nt1 + nt2) + ncomb);
           wg_release();
           wg_push(c, NR, [&](int i) { return NR + 1 + i; },    // the grouping tasks
                   [&](int i) { return i; });
@@ -811,7 +818,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       // dynamic: every expert event receives all of its rows at once (its
       // data-dependent wait count) and fires; the fired experts' task ranges
       // together are the whole gate/up range, pushed in one piece
-      set_total(c, NR + nb * (nt1 + nt2) + (kInlineCombine ? 0 : ncomb));
+      set_total(c, NR + nb * (nt1 + nt2) + ncomb);
       for (int e = tid; e < m.E; e += kThreads) {
         const int n = ld_coh(&m.counts[e]);
         if (n > 0) {
