@@ -189,7 +189,9 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   // LDS and no global round trip or store-completion wait separates them
   const bool solo_route = NR == 1 && inline_group;
   const int wc = m.k;   // EV_C wait count: the k rows of a token, one per down column tile
-  const bool inline_comb = (sched == ET_SCHED_STATIC || sched == ET_SCHED_DYNAMIC) &&
+  // (compiled into the 16-row variant only, the one tiny token counts use:
+  // the extra path measurably slowed the other variants' down tiles)
+  const bool inline_comb = TV == TV_M16 && (sched == ET_SCHED_STATIC || sched == ET_SCHED_DYNAMIC) &&
                            m.T <= kInlineCombineTokens;
   const int ncomb = inline_comb ? 0 : cdiv(m.T, kCombTok) * cdiv(m.H, m.ccols);   // combine tiles
 
@@ -720,7 +722,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     }
     if (sched == ET_SCHED_PER_OP) return true;
     wg_release();
-    if (!inline_comb) {
+    if (TV != TV_M16 || !inline_comb) {
       if (sched != ET_SCHED_DYNAMIC) {
         t0_notify(c, EV_DOWN, 1, meta(MD_TOTAL2), task);
       } else if (wg_notify(c, EV_DOWN, 1, meta(MD_TOTAL2), task)) {
