@@ -62,7 +62,7 @@ struct MoeArgs {
   int* perm;
   int* inv;
   uint16_t* h;
-  float* y;
+  uint16_t* y;       // [T*k, H] bf16 down-projection rows (workspace)
   int T, H, I, E, k, NR, tpr;
   int ccols;           // combine tile columns
   int ev_exp, ev_he, ev_h, ev_c;
@@ -231,15 +231,16 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     n = l / nblk;
     gb = c_blk[e] + l % nblk;
   };
-  const Rsrc ry = make_rsrc(m.y, (uint32_t)((size_t)m.T * m.k * m.H * 4));
+  const Rsrc ry = make_rsrc(m.y, (uint32_t)((size_t)m.T * m.k * m.H * 2));
 
   // Combine for ntok tokens (token of list entry i: tok_of(i)) over columns
   // [c0, c0 + ncols): out[t, col] = sum_{s<k} w[t, s] * y[inv[t, s], col],
-  // accumulated in slot order with one fused multiply-add per slot.  The
-  // (w, position) pairs are staged in LDS first; each thread then owns 4
-  // columns of one or two items and issues all their 16-byte row loads
-  // before summing, so a pass costs one memory round trip.  The dynamic (inline) and tiled (static)
-  // combines share this code and give bit-identical results.
+  // accumulated in fp32 in slot order with one fused multiply-add per slot
+  // (the y rows are bf16).  The (w, position) pairs are staged in LDS first;
+  // each thread then owns 8 columns of one or two items and issues all their
+  // 16-byte row loads before summing, so a pass costs one memory round trip.
+  // The inline and tiled combines share this code and give bit-identical
+  // results.
   auto combine = [&](int ntok, auto tok_of, int c0, int ncols, float* cw, int* cp) ET_INLINE {
     const int k = m.k;
     for (int i = tid; i < ntok * k; i += kThreads) {
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       cp[i] = ld_coh(&m.inv[t * k + s]);
     }
     __syncthreads();
-    const int nq = ncols / 4;              // 4 columns (16 bytes) per item
+    const int nq = ncols / 8;              // 8 columns (16 bytes of bf16) per item
     const int nit = ntok * nq;
     // IT items per thread per pass, all KM * IT row loads issued before any
     // sum (IT = 2 when k <= 8 keeps the loads within 64 registers)
@@ -259,28 +260,33 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
 #pragma unroll
         for (int u = 0; u < IT; ++u) {
           const int i = i0 + u * kThreads;
-          const int ti = i / nq, col = c0 + 4 * (i % nq);
+          const int ti = i / nq, col = c0 + 8 * (i % nq);
 #pragma unroll
           for (int s = 0; s < KM; ++s)
-            if (s < k && i < nit) yv[u][s] = ld16c(ry, (uint32_t)((cp[ti * k + s] * (size_t)m.H + col) * 4));
+            if (s < k && i < nit) yv[u][s] = ld16c(ry, (uint32_t)((cp[ti * k + s] * (size_t)m.H + col) * 2));
         }
 #pragma unroll
         for (int u = 0; u < IT; ++u) {
           const int i = i0 + u * kThreads;
           if (i >= nit) break;
-          const int ti = i / nq, col = c0 + 4 * (i % nq);
-          float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+          const int ti = i / nq, col = c0 + 8 * (i % nq);
+          float acc[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[q] = 0.f;
 #pragma unroll
           for (int s = 0; s < KM; ++s)
             if (s < k) {
               const float w = cw[ti * k + s];
-              const f32x4 y4 = __builtin_bit_cast(f32x4, yv[u][s]);
-              acc.x = __fmaf_rn(w, y4[0], acc.x);
-              acc.y = __fmaf_rn(w, y4[1], acc.y);
-              acc.z = __fmaf_rn(w, y4[2], acc.z);
-              acc.w = __fmaf_rn(w, y4[3], acc.w);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const uint32_t two = (uint32_t)yv[u][s][q];   // two bf16: low half first
+                acc[2 * q] = __fmaf_rn(w, __builtin_bit_cast(float, two << 16), acc[2 * q]);
+                acc[2 * q + 1] = __fmaf_rn(w, __builtin_bit_cast(float, two & 0xffff0000u), acc[2 * q + 1]);
+              }
             }
-          *reinterpret_cast<float4*>(m.out + (size_t)tok_of(ti) * m.H + col) = acc;
+          float4* o = reinterpret_cast<float4*>(m.out + (size_t)tok_of(ti) * m.H + col);
+          o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+          o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
         }
       }
     };
@@ -682,7 +688,9 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     if (!ok) return false;
     if constexpr (kWide) {
       // y staged 32 rows at a time in the (now idle) ring slot, then written
-      // out with 16-byte coherent stores, 64 per 256-column row
+      // out as bf16 with 16-byte coherent stores, 32 per 256-column row (the
+      // coherent stores write through to memory at ~7 GB/s per CU: halving
+      // y's bytes cut the down tiles' store time in half)
       constexpr int kYs = bn2 + 4;                 // padded row (floats)
       float* yl = reinterpret_cast<float*>(s0);
       const int nrow = pend - pos0;
@@ -699,11 +707,15 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
                     tile.acc[2 * q + mm][j][r];
           lds_barrier();
           const int nr = min(32, nrow - 32 * q);
-          constexpr int kCpr = bn2 / 4;            // 16-byte chunks per row
+          constexpr int kCpr = bn2 / 8;            // 16-byte chunks (8 bf16) per row
           for (int i = tid; i < nr * kCpr; i += kThreads) {
             const int row = i / kCpr, ch = i % kCpr;
-            st16c(ry, (uint32_t)((pos0 + 32 * q + row) * m.H + n2 * bn2 + 4 * ch) * 4u,
-                  *reinterpret_cast<const i32x4*>(yl + row * kYs + 4 * ch));
+            const float* f = yl + row * kYs + 8 * ch;
+            i32x4 v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              v[q] = (int)((uint32_t)f32_to_bf16(f[2 * q]) | ((uint32_t)f32_to_bf16(f[2 * q + 1]) << 16));
+            st16c(ry, (uint32_t)((pos0 + 32 * q + row) * m.H + n2 * bn2 + 8 * ch) * 2u, v);
           }
           lds_barrier();   // the stores stay in flight
         }
@@ -717,7 +729,8 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
             if (r == wave) {
               const int pos = pos0 + 16 * mt + 4 * (lane >> 4) + r;
               if (pos < pend)
-                st_coh(&m.y[(size_t)pos * m.H + n2 * bn2 + cw + 16 * j + (lane & 15)], tile.acc[mt][j][r]);
+                st_coh(&m.y[(size_t)pos * m.H + n2 * bn2 + cw + 16 * j + (lane & 15)],
+                       f32_to_bf16(tile.acc[mt][j][r]));
             }
     }
     if (sched == ET_SCHED_PER_OP) return true;
@@ -993,7 +1006,7 @@ int launch_moe(const LaunchCommon& lc, const float* logits, const uint16_t* x, i
   m.perm = reinterpret_cast<int*>(aux + ax.perm);
   m.inv = reinterpret_cast<int*>(aux + ax.inv);
   m.h = reinterpret_cast<uint16_t*>(aux + ax.h);
-  m.y = reinterpret_cast<float*>(aux + ax.y);
+  m.y = reinterpret_cast<uint16_t*>(aux + ax.y);
   m.T = T;
   m.H = p->hidden;
   m.I = p->inter;

@@ -190,7 +190,7 @@ inline MoeAux moe_aux_layout(const MoePlan& p) {
   a.perm = take(TK * 4);
   a.inv = take(TK * 4);
   a.h = take(TK * p.inter * 2);
-  a.y = take(TK * p.hidden * 4);
+  a.y = take(TK * p.hidden * 2);   // bf16 down-projection rows
   a.bytes = o;
   return a;
 }

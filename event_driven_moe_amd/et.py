@@ -262,7 +262,7 @@ def moe_aux(ws, T, intermediates=False):
     }
     if intermediates:
         aux["h"] = ws.view(lay.h, torch.bfloat16, T * k * ws.plan.inter).view(T * k, ws.plan.inter)
-        aux["y"] = ws.view(lay.y, torch.float32, T * k * ws.plan.hidden).view(T * k, ws.plan.hidden)
+        aux["y"] = ws.view(lay.y, torch.bfloat16, T * k * ws.plan.hidden).view(T * k, ws.plan.hidden)
     return aux
 
 

@@ -138,7 +138,7 @@ typedef struct et_layout {
   size_t inv;               /* MoE: int32 [T, k], inv[t, s] = pos */
   size_t task_indptr;       /* MoE: int32 [E+1] gate/up tasks per expert (CSR) */
   size_t h;                 /* MLP: bf16 [B, I]; MoE: bf16 [T*k, I] (grouped rows) */
-  size_t y;                 /* MoE: float [T*k, H] down-projection rows (grouped rows) */
+  size_t y;                 /* MoE: bf16 [T*k, H] down-projection rows (grouped rows) */
 } et_layout;
 
 /* Device-side state of a workspace, read back by et_read_status(). */

@@ -137,9 +137,11 @@ def test_event_invariants(sched, T):
 
 def _exact_case(k, E=4, H=256, I=256, T=50, seed=0):
     """Integer experts: x in {0,1} with x[:,0]=1; gate row 0 in [16,40) so
-    SiLU(g) == g below bf16 precision; |u| <= 6, so h = g*u exactly; down in
-    {-2..2}: every y is an exact fp32 integer.  Logits make the kept weights
-    exactly 1 (k = 1) or 1/2 (two tied maxima, k = 2)."""
+    SiLU(g) == g below bf16 precision; |u| <= 3, so h = g*u exactly (|h| <=
+    117); two +-1 entries per down column, so every y is an integer with
+    |y| <= 234, exact in bf16 (the layer keeps y, the down projection's rows,
+    in bf16 like h).  Logits make the kept weights exactly 1 (k = 1) or 1/2
+    (two tied maxima, k = 2)."""
     g = torch.Generator(device="cpu").manual_seed(seed)
     x = torch.randint(0, 2, (T, H), generator=g).float()
     x[:, 0] = 1
@@ -148,9 +150,13 @@ def _exact_case(k, E=4, H=256, I=256, T=50, seed=0):
     wu = torch.zeros(E, H, I)
     for e in range(E):
         for i in range(I):
-            r = torch.randperm(H - 1, generator=g)[:6] + 1
-            wu[e, r, i] = torch.randint(0, 2, (6,), generator=g).float() * 2 - 1
-    wd = torch.randint(-2, 3, (E, I, H), generator=g).float()
+            r = torch.randperm(H - 1, generator=g)[:3] + 1
+            wu[e, r, i] = torch.randint(0, 2, (3,), generator=g).float() * 2 - 1
+    wd = torch.zeros(E, I, H)
+    for e in range(E):
+        for j in range(H):
+            r = torch.randperm(I, generator=g)[:2]
+            wd[e, r, j] = torch.randint(0, 2, (2,), generator=g).float() * 2 - 1
     logits = torch.randn(T, E, generator=g) - 4.0
     for t in range(T):
         logits[t, torch.randperm(E, generator=g)[:k]] = 1.0   # ties between k distinct experts
