@@ -504,14 +504,15 @@ __device__ __forceinline__ f32x4 mfma16(i32x4 a, i32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// fp32 -> bf16, round to nearest even (gfx950's conversion instruction)
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);   // NaN stays NaN
-  u += 0x7fffu + ((u >> 16) & 1u);                                             // nearest-even
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// SiLU with the hardware reciprocal (about 1 ulp in fp32): its result is
+// rounded to bf16 next, so the IEEE division's extra accuracy is never seen,
+// and the division's instruction sequence dominated the gate/up epilogue.
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // Sum over each 16-lane row, result in every lane of the row (quad
 // permutes, then the half-row and row mirrors).

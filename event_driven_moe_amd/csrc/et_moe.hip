@@ -687,12 +687,10 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       ok = tile.run(rh, rows_off, rb, bo, m.I / kKBlock, gate, reinterpret_cast<float*>(s0));
     if (!ok) return false;
     if constexpr (kWide) {
-      // y staged 32 rows at a time in the (now idle) ring slot, then written
-      // out as bf16 with 16-byte coherent stores, 32 per 256-column row (the
-      // coherent stores write through to memory at ~7 GB/s per CU: halving
-      // y's bytes cut the down tiles' store time in half)
-      constexpr int kYs = bn2 + 4;                 // padded row (floats)
-      float* yl = reinterpret_cast<float*>(s0);
+      // y staged as bf16, 32 rows at a time, in the (now idle) ring slot, then
+      // written out with 16-byte coherent stores, 32 per 256-column row
+      constexpr int kYs = bn2 + 8;                 // padded row (elements)
+      uint16_t* yl = reinterpret_cast<uint16_t*>(s0);
       const int nrow = pend - pos0;
 #pragma unroll
       for (int q = 0; q < MT / 2; ++q)
@@ -704,18 +702,14 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
 #pragma unroll
               for (int r = 0; r < 4; ++r)
                 yl[(16 * mm + 4 * (lane >> 4) + r) * kYs + cw + 16 * j + (lane & 15)] =
-                    tile.acc[2 * q + mm][j][r];
+                    f32_to_bf16(tile.acc[2 * q + mm][j][r]);
           lds_barrier();
           const int nr = min(32, nrow - 32 * q);
           constexpr int kCpr = bn2 / 8;            // 16-byte chunks (8 bf16) per row
           for (int i = tid; i < nr * kCpr; i += kThreads) {
             const int row = i / kCpr, ch = i % kCpr;
-            const float* f = yl + row * kYs + 8 * ch;
-            i32x4 v;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              v[q] = (int)((uint32_t)f32_to_bf16(f[2 * q]) | ((uint32_t)f32_to_bf16(f[2 * q + 1]) << 16));
-            st16c(ry, (uint32_t)((pos0 + 32 * q + row) * m.H + n2 * bn2 + 8 * ch) * 2u, v);
+            st16c(ry, (uint32_t)((pos0 + 32 * q + row) * m.H + n2 * bn2 + 8 * ch) * 2u,
+                  *reinterpret_cast<const i32x4*>(yl + row * kYs + 8 * ch));
           }
           lds_barrier();   // the stores stay in flight
         }
