@@ -384,7 +384,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     using std::integral_constant;
     if (m.E <= 64) route_tokens(integral_constant<int, 1>{}, integral_constant<int, 4>{});
     else if (m.E <= 128) route_tokens(integral_constant<int, 2>{}, integral_constant<int, 4>{});
-    else if (m.E <= 256) route_tokens(integral_constant<int, 4>{}, integral_constant<int, 2>{});
+    else if (m.E <= 256) route_tokens(integral_constant<int, 4>{}, integral_constant<int, 4>{});
     else route_tokens(integral_constant<int, kMaxExperts / 64>{}, integral_constant<int, 1>{});
     lds_barrier();   // the histogram is complete; the id and weight stores stay in flight
     if (!solo_route)
