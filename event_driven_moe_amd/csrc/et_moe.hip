@@ -687,32 +687,32 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       ok = tile.run(rh, rows_off, rb, bo, m.I / kKBlock, gate, reinterpret_cast<float*>(s0));
     if (!ok) return false;
     if constexpr (kWide) {
-      // y staged as bf16, 32 rows at a time, in the (now idle) ring slot, then
-      // written out with 16-byte coherent stores, 32 per 256-column row
+      // y staged as bf16 in the (now idle) ring slots -- rows 0..63 in s0,
+      // 64..127 in s1, one pass -- then written out with 16-byte coherent
+      // stores, 32 per 256-column row
       constexpr int kYs = bn2 + 8;                 // padded row (elements)
-      uint16_t* yl = reinterpret_cast<uint16_t*>(s0);
+      static_assert(64 * kYs * 2 <= kSlot, "64 staged rows per ring slot");
       const int nrow = pend - pos0;
 #pragma unroll
-      for (int q = 0; q < MT / 2; ++q)
-        if (32 * q < nrow) {
+      for (int mt = 0; mt < MT; ++mt)
+        if (16 * mt < nrow) {
+          uint16_t* yl = reinterpret_cast<uint16_t*>(mt < 4 ? s0 : s1);
 #pragma unroll
-          for (int mm = 0; mm < 2; ++mm)
+          for (int j = 0; j < Cfg::NB2; ++j)
 #pragma unroll
-            for (int j = 0; j < Cfg::NB2; ++j)
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                yl[(16 * mm + 4 * (lane >> 4) + r) * kYs + cw + 16 * j + (lane & 15)] =
-                    f32_to_bf16(tile.acc[2 * q + mm][j][r]);
-          lds_barrier();
-          const int nr = min(32, nrow - 32 * q);
-          constexpr int kCpr = bn2 / 8;            // 16-byte chunks (8 bf16) per row
-          for (int i = tid; i < nr * kCpr; i += kThreads) {
-            const int row = i / kCpr, ch = i % kCpr;
-            st16c(ry, (uint32_t)((pos0 + 32 * q + row) * m.H + n2 * bn2 + 8 * ch) * 2u,
-                  *reinterpret_cast<const i32x4*>(yl + row * kYs + 8 * ch));
-          }
-          lds_barrier();   // the stores stay in flight
+            for (int r = 0; r < 4; ++r)
+              yl[(16 * (mt % 4) + 4 * (lane >> 4) + r) * kYs + cw + 16 * j + (lane & 15)] =
+                  f32_to_bf16(tile.acc[mt][j][r]);
         }
+      lds_barrier();
+      constexpr int kCpr = bn2 / 8;                // 16-byte chunks (8 bf16) per row
+      for (int i = tid; i < nrow * kCpr; i += kThreads) {
+        const int row = i / kCpr, ch = i % kCpr;
+        const uint16_t* yl = reinterpret_cast<const uint16_t*>(row < 64 ? s0 : s1);
+        st16c(ry, (uint32_t)((pos0 + row) * m.H + n2 * bn2 + 8 * ch) * 2u,
+              *reinterpret_cast<const i32x4*>(yl + (row % 64) * kYs + 8 * ch));
+      }
+      lds_barrier();     // the ring slots are refilled by the next task; the stores stay in flight
     } else {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
