@@ -551,13 +551,16 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // fold the rows into lane 63, which is read back as a uniform value.
 template <bool MAX>
 __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x) {
+  // the lanes a step leaves out (row masks) receive the operation's identity
+  // (0 for max, all ones for min), so each step compiles to one DPP max/min
   auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xf, 0xf, false));  // quad [1,0,3,2]
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xf, 0xf, false));  // quad [2,3,0,1]
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xf, 0xf, false)); // row half mirror
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x140, 0xf, 0xf, false)); // row mirror
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x142, 0xa, 0xf, false)); // row bcast 15
-  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x143, 0xc, 0xf, false)); // row bcast 31
+  constexpr int id = MAX ? 0 : -1;
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0xB1, 0xf, 0xf, false));  // quad [1,0,3,2]
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x4E, 0xf, 0xf, false));  // quad [2,3,0,1]
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x141, 0xf, 0xf, false)); // row half mirror
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x140, 0xf, 0xf, false)); // row mirror
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x142, 0xa, 0xf, false)); // row bcast 15
+  x = op(x, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)x, 0x143, 0xc, 0xf, false)); // row bcast 31
   return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 

@@ -310,22 +310,31 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     __syncthreads();
     const int t0 = r * m.tpr;
     const int t1 = min(m.T, t0 + m.tpr);
+    const Rsrc rlog = make_rsrc(m.logits, (uint32_t)m.T * m.E * 4u);
     // NJ keys per lane (E <= 64 NJ); the logits of NB tokens of this wave
     // (t0 + wave, t0 + wave + 4, ...) are requested before any is ranked
     auto route_tokens = [&](auto nj_c, auto nb_c) ET_INLINE {
       constexpr int NJ = decltype(nj_c)::value, NB = decltype(nb_c)::value;
       for (int tb = t0 + wave; tb < t1; tb += 4 * NB) {
+        // buffer loads without branches, all in flight together; lanes past
+        // the chunk or past E read out of range and take key 0, below every
+        // real key
         uint32_t kb[NB][NJ];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const int t = tb + 4 * b;
-          const float* lg = m.logits + (size_t)t * m.E;
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int j = 0; j < NJ; ++j) {
-            const int e = lane + 64 * j;
-            kb[b][j] = (t < t1 && e < m.E) ? route_key32(lg[e]) : 0u;   // 0: below every key
+            const int t = tb + 4 * b, e = lane + 64 * j;
+            const bool ok = t < t1 && e < m.E;
+            kb[b][j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                rlog, ok ? (t * m.E + e) * 4 : (int)kOOB, 0, 0);
           }
-        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            kb[b][j] = (tb + 4 * b < t1 && lane + 64 * j < m.E)
+                           ? route_key32(__builtin_bit_cast(float, kb[b][j])) : 0u;
         // the NB tokens' k rounds are interleaved: their wave reductions are
         // independent chains that the scheduler overlaps
         uint32_t taken[NB], my_key[NB], key0[NB];
@@ -400,20 +409,16 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     int* part = tmp + 8;                   // [256] chunk sums
     const int n_ne = cdiv(m.T, m.tpr);
     const int tot = n_ne * m.E;
-    // all histogram loads in flight at once (16 per thread per pass); a solo
-    // routing chunk left its histogram in hs already
-    for (int b0 = 0; !solo_route && b0 < tot; b0 += 16 * kThreads) {
-      int v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int i = b0 + u * kThreads + tid;
-        v[u] = i < tot ? ld_coh(&m.hist[i]) : 0;
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int i = b0 + u * kThreads + tid;
-        if (i < tot) hs[i] = v[u];
-      }
+    // the histograms copied straight into LDS (coherent 16-byte copies that
+    // take no registers, all in flight at once: at most 8 1 KB chunks per
+    // wave); a solo routing chunk left its histogram in hs already
+    const Rsrc rhist = make_rsrc(m.hist, (uint32_t)(4 * tot + 15) & ~15u);
+    const int nv = tot / 4;
+    static_assert(kHistEntries <= 4 * 8 * 256, "8 chunk copies per wave");
+    if (!solo_route) {
+      for (int ch = wave; ch < cdiv(tot, 256); ch += 4)
+        dma16<true>(rhist, hs + 256 * ch, (uint32_t)(1024 * ch + 16 * lane));
+      wait_mem();
     }
     __syncthreads();
     // per-expert prefix over the chunks r: P threads per expert, each summing
@@ -425,6 +430,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     for (int q = tid; q < m.E * P; q += kThreads) {
       const int e = q / P, p = q % P;
       int acc = 0;
+#pragma unroll 8
       for (int r = p * span; r < min(n_ne, (p + 1) * span); ++r) acc += hs[r * m.E + e];
       part[q % kThreads] = acc;
     }
@@ -433,6 +439,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       const int e = q / P, p = q % P;
       int run = 0;
       for (int pp = 0; pp < p; ++pp) run += part[(e * P + pp) % kThreads];
+#pragma unroll 8
       for (int r = p * span; r < min(n_ne, (p + 1) * span); ++r) {
         const int v = hs[r * m.E + e];
         hs[r * m.E + e] = run;
@@ -457,7 +464,17 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       st_coh(&m.blk_indptr[m.E], nb);
       st_coh(&m.task_indptr[m.E], nb * nt1);
     }
-    for (int i = tid; i < tot; i += kThreads) st_coh(&m.hist[i], hs[i] + cnt[i % m.E]);
+    // chunk bases hist[r, e] = tok_indptr[e] + rows of e in chunks before r,
+    // four per 16-byte store (the four share a chunk when E % 4 == 0)
+    if (m.E % 4 == 0) {
+      for (int i = tid; i < nv; i += kThreads) {
+        const int e = (4 * i) % m.E;
+        const i32x4 h = *reinterpret_cast<const i32x4*>(hs + 4 * i);
+        st16c(rhist, 16u * i, i32x4{h[0] + cnt[e], h[1] + cnt[e + 1], h[2] + cnt[e + 2], h[3] + cnt[e + 3]});
+      }
+    } else {
+      for (int i = tid; i < tot; i += kThreads) st_coh(&m.hist[i], hs[i] + cnt[i % m.E]);
+    }
     if (tid == 0) {
       st_rlx(&ra.hdr[HDR_META + MD_NB], nb);
       st_rlx(&ra.hdr[HDR_META + MD_TOTAL1], nb * nt1);
