@@ -194,6 +194,26 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   const bool inline_comb = TV == TV_M16 && (sched == ET_SCHED_STATIC || sched == ET_SCHED_DYNAMIC) &&
                            m.T <= kInlineCombineTokens;
   const int ncomb = inline_comb ? 0 : cdiv(m.T, kCombTok) * cdiv(m.H, m.ccols);   // combine tiles
+  // Static schedule with at least kCombGroupMin token groups and at most
+  // kCombGroupRounds down tiles per workgroup: each combine tile waits on its
+  // own event E_cg[token group, column tile] instead of the last down tile,
+  // so combine tiles overlap the down tiles' tail.  With fewer groups each
+  // group's rows reach nearly every active expert and its event fires only
+  // at the end; with deeper down phases (and in the dynamic schedule, where
+  // each down tile would have to push the tiles it completes) the notifies
+  // cost more than the overlap saves.  Otherwise the combine waits on
+  // EV_DOWN.
+  auto comb_groups = [&](int total2) ET_INLINE {
+    return sched == ET_SCHED_STATIC && !inline_comb && cdiv(m.T, kCombTok) >= kCombGroupMin &&
+           total2 <= kCombGroupRounds * c.G;
+  };
+  // wait count of E_cg[tc, cc]: k rows per token of the group, times the down
+  // column tiles overlapping the combine tile's columns
+  auto comb_wait = [&](int tc, int cc) ET_INLINE {
+    const int ntok = min(m.T, (tc + 1) * kCombTok) - tc * kCombTok;
+    const int c0 = cc * m.ccols, c1 = min(m.H, c0 + m.ccols);
+    return ntok * m.k * ((c1 - 1) / bn2 - c0 / bn2 + 1);
+  };
 
   // LDS carve-outs (task kinds never overlap in time inside one workgroup)
   int* s_i = reinterpret_cast<int*>(s0);                              // route / scan / group
@@ -664,7 +684,8 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     return true;
   };
 
-  auto gemm2 = [&](int t2g, int task) ET_INLINE -> bool {
+  auto gemm2 = [&](int t2g, int task, int total2) ET_INLINE -> bool {
+    const bool cgrp = comb_groups(total2);
     load_cache();
     int e, n2, gb, pos0, pend;
     decode(t2g, nt2, e, n2, gb);
@@ -703,6 +724,15 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     else
       ok = tile.run(rh, rows_off, rb, bo, m.I / kKBlock, gate, reinterpret_cast<float*>(s0));
     if (!ok) return false;
+    // The combine-group notifies need each row's token: the block's perm
+    // entries are copied into LDS now (wave 0, 16 bytes per lane, no
+    // registers) and arrive while the y rows are staged and stored.  Slot s2
+    // is idle after the ring tile; the stream tiles leave s1 unused.
+    int* grp = reinterpret_cast<int*>(kWide ? s2 : s1);   // [rows]
+    if (cgrp && wave == 0) {
+      const Rsrc rperm = make_rsrc(m.perm, (uint32_t)m.T * m.k * 4u);
+      dma16<true>(rperm, grp, 4 * lane < pend - pos0 ? (uint32_t)(pos0 + 4 * lane) * 4u : kOOB);
+    }
     if constexpr (kWide) {
       // y staged as bf16 in the (now idle) ring slots -- rows 0..63 in s0,
       // 64..127 in s1, one pass -- then written out with 16-byte coherent
@@ -745,17 +775,36 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
             }
     }
     if (sched == ET_SCHED_PER_OP) return true;
-    wg_release();
-    if (TV != TV_M16 || !inline_comb) {
+    wg_release();   // also completes wave 0's perm copy
+    if (!cgrp && !inline_comb) {
       if (sched != ET_SCHED_DYNAMIC) {
-        t0_notify(c, EV_DOWN, 1, meta(MD_TOTAL2), task);
-      } else if (wg_notify(c, EV_DOWN, 1, meta(MD_TOTAL2), task)) {
+        t0_notify(c, EV_DOWN, 1, total2, task);
+      } else if (wg_notify(c, EV_DOWN, 1, total2, task)) {
         // the last down tile: push the combine tiles
-        const int b3 = base1 + meta(MD_TOTAL1) + meta(MD_TOTAL2);
+        const int b3 = base1 + meta(MD_TOTAL1) + total2;
         wg_push(c, ncomb, [&](int i) { return b3 + i; }, [&](int i) { return i; });
       }
       return true;
     }
+    if (cgrp) {
+      // Data-dependent notify targets: the block's rows are in token order,
+      // so the tokens of each combine group form one run of rows; the first
+      // row of a run decrements E_cg[group, c] by the run's length for each
+      // combine column tile c this tile's columns overlap.
+      const int nrow = pend - pos0;
+      const int g = tid < nrow ? grp[tid] / m.k / kCombTok : -1;
+      if (tid < nrow && (tid == 0 || grp[tid - 1] / m.k / kCombTok != g)) {
+        int len = 1;
+        while (tid + len < nrow && grp[tid + len] / m.k / kCombTok == g) ++len;
+        const int ncol = cdiv(m.H, m.ccols);
+        const int cc1 = min(ncol - 1, ((n2 + 1) * bn2 - 1) / m.ccols);
+        for (int cc = n2 * bn2 / m.ccols; cc <= cc1; ++cc)
+          __hip_atomic_fetch_add(c.ev + m.ev_c + g * ncol + cc, -len, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
+      return true;
+    }
+    if constexpr (TV != TV_M16) return true;   // inline combine: 16-row stream tiles only
     // one notify per row on EV_C[token, n2] (wait count k); the notify that
     // completes a token's k rows for this column tile runs its combine
     if (tid == 0) sh.v[5] = 0;
@@ -778,13 +827,15 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     return true;
   };
 
-  auto combine_tile = [&](int t3, int task) ET_INLINE -> bool {
-    if ((sched == ET_SCHED_STATIC || sched == ET_SCHED_BARRIER) && !seen_down) {
+  auto combine_tile = [&](int t3, int task, int total2) ET_INLINE -> bool {
+    const int ncol = cdiv(m.H, m.ccols);
+    const int tc = t3 / ncol, cc = t3 % ncol;
+    if (comb_groups(total2)) {
+      if (!wg_wait(c, m.ev_c + t3, comb_wait(tc, cc), task)) return false;
+    } else if ((sched == ET_SCHED_STATIC || sched == ET_SCHED_BARRIER) && !seen_down) {
       if (!wg_wait(c, EV_DOWN, meta(MD_TOTAL2), task)) return false;
       seen_down = true;
     }
-    const int ncol = cdiv(m.H, m.ccols);
-    const int tc = t3 / ncol, cc = t3 % ncol;
     const int t0 = tc * kCombTok;
     const int ntok = min(m.T, t0 + kCombTok) - t0;
     const int c0 = cc * m.ccols;
@@ -924,8 +975,8 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     }
     const int total1 = meta(MD_TOTAL1), total2 = meta(MD_TOTAL2);
     if (task < base1 + total1) return gemm1(task - base1, task);
-    if (task < base1 + total1 + total2) return gemm2(task - base1 - total1, task);
-    return combine_tile(task - base1 - total1 - total2, task);
+    if (task < base1 + total1 + total2) return gemm2(task - base1 - total1, task, total2);
+    return combine_tile(task - base1 - total1 - total2, task, total2);
   };
 
   if (sched == ET_SCHED_DYNAMIC) {

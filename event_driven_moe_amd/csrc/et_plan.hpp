@@ -119,18 +119,25 @@ struct MlpPlan {
 //   EV_SCAN   scan done                   (1)
 //   EV_GROUP  all grouping tasks done     (n_route)
 //   EV_G1ALL  all gate/up tasks done      (total1)        [barrier mode]
-//   EV_DOWN   all down tasks done         (total2)        [barrier]
+//   EV_DOWN   all down tasks done         (total2)        [without EV_CG]
 //   EV_EXP[e] rows of expert e grouped    (counts[e])     data-dependent
 //   EV_HE[e]  gate/up tiles of expert e   (blocks[e] * inter / bn1) data-dependent [dynamic]
 //   EV_H[gb]  gate/up tiles of block gb   (inter / bn1)                    [static]
-//   EV_C[t][c] down tiles covering token t, column tile c (top_k) [static, dynamic]
+//   EV_C[t][c] down tiles covering token t, column tile c (top_k) [inline combine]
+//   EV_CG[g][c] (same base as EV_C; combine tiles) rows of the kCombTok tokens
+//             of group g times down column tiles overlapping combine column
+//             tile c (top_k * tokens * tiles)  [static; groups >= kCombGroupMin,
+//             down tiles <= kCombGroupRounds * G]
 // tasks: [0, R) routing, R scan, [R+1, 2R+1) grouping, then total1 gate/up
-//   tiles (block-major, column tile fastest), total2 down tiles, then (barrier,
-//   per-op) combine tiles of kCombTok tokens x kCombCols columns.
+//   tiles (block-major, column tile fastest), total2 down tiles, then the
+//   combine tiles of kCombTok tokens x ccols columns (none when the combine
+//   runs inline in the down tiles).
 // ---------------------------------------------------------------------------
 constexpr int kCombTok = 16;
 constexpr int kCombCols = 256;      // combine tile columns (64 when 256 gives fewer tiles than CUs)
 constexpr int kCombColsMin = 64;
+constexpr int kCombGroupRounds = 4;   // static: E_cg when down tiles <= this many per workgroup
+constexpr int kCombGroupMin = 16;     //   and at least this many token groups
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kHistEntries = 8192;    // n_route * E must fit (int32, 32 KB of LDS)
@@ -150,7 +157,10 @@ struct MoePlan {
   ET_HD int ev_h() const { return EV_FIXED + 2 * n_experts; }
   ET_HD int ev_c() const { return ev_h() + nb_max(); }
   ET_HD int n_events_max() const { return ev_c() + t_max * (hidden / kMinCols); }
-  ET_HD int extent(int T, const Tiling& t) const { return ev_c() + T * (hidden / t.bn2); }
+  ET_HD int extent(int T, const Tiling& t) const {
+    const int c = T * (hidden / t.bn2), g = cdiv(T, kCombTok) * cdiv(hidden, kCombColsMin);
+    return ev_c() + (c > g ? c : g);
+  }
   ET_HD int n_comb(int T) const { return cdiv(T, kCombTok) * cdiv(hidden, kCombColsMin); }
   ET_HD int max_tasks() const {
     return 2 * n_route + 1 + nb_max() * (inter / kMinCols + hidden / kMinCols) + n_comb(t_max);

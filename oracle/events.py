@@ -77,18 +77,27 @@ def mlp_table(batch, hidden, inter, rows_per_tile, gate_cols, h_tile, down_cols,
     return tab
 
 
-def moe_table(counts, rows_per_tile, inter, gate_cols, hidden, down_cols, n_route):
+def moe_table(counts, rows_per_tile, inter, gate_cols, hidden, down_cols, n_route,
+              tokens=None, top_k=None, comb_tok=16, comb_cols=None):
     """MoE layer under a tiling: ``n_route`` routing tasks, one scan task,
     ``n_route`` grouping tasks; expert e owns ceil(counts[e]/rows) row blocks;
     each block has inter/gate_cols gate/up tiles and hidden/down_cols down
     tiles.  E_exp[e] starts at counts[e] (data-dependent); E_h[block] at the
     number of gate/up tiles of a block; E_he[e] (the dynamic schedule's
     per-expert edge from gate/up to down tiles) at the number of gate/up
-    tiles over all of expert e's blocks (data-dependent)."""
+    tiles over all of expert e's blocks (data-dependent).
+
+    With ``tokens`` given: E_cg[g, c], the edge from the down tiles to the
+    combine tile of tokens [g*comb_tok, (g+1)*comb_tok) and columns
+    [c*comb_cols, (c+1)*comb_cols).  Each down tile notifies it once per row
+    of its block that belongs to a token of group g (a notify target read
+    from the run-time permutation) when the tile's columns overlap the
+    combine tile's, so it starts at top_k rows per token of the group times
+    the number of down column tiles overlapping the combine tile."""
     counts = np.asarray(counts, dtype=np.int64)
     blocks = -(-counts // rows_per_tile)
     nb = int(blocks.sum())
-    return {
+    tab = {
         "tasks": {
             "route": n_route, "scan": 1, "group": n_route,
             "gate_up": nb * (inter // gate_cols),
@@ -103,6 +112,16 @@ def moe_table(counts, rows_per_tile, inter, gate_cols, hidden, down_cols, n_rout
                      "wait_count": blocks * (inter // gate_cols)},
         },
     }
+    if tokens is not None:
+        ng, nc = -(-tokens // comb_tok), -(-hidden // comb_cols)
+        g0 = np.arange(ng) * comb_tok
+        ntok = np.minimum(tokens, g0 + comb_tok) - g0
+        c0 = np.arange(nc) * comb_cols
+        c1 = np.minimum(hidden, c0 + comb_cols)
+        ndown = (c1 - 1) // down_cols - c0 // down_cols + 1
+        tab["events"]["E_cg"] = {"shape": (ng, nc),
+                                 "wait_count": np.outer(ntok * top_k, ndown).astype(np.int64)}
+    return tab
 
 
 def notify_counts(producer_map, shape):

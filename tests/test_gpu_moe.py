@@ -97,13 +97,14 @@ def test_fetch_batches(fetch):
     check_against_oracle("moe_skewed", 256, out, aux)
 
 
-@pytest.mark.parametrize("T", [256, 1024])
+@pytest.mark.parametrize("T", [16, 64, 256, 1024])
 @pytest.mark.parametrize("sched", ["static", "dynamic"])
 def test_event_invariants(sched, T):
     """Each task ran once; the data-dependent expert events ended at their
     run-time wait counts (rows routed to each expert; dynamic: also the
     gate/up tiles over each expert's blocks), the static schedule's block
-    events at the number of gate/up tiles of a block."""
+    events at the number of gate/up tiles of a block, and every combine
+    tile's event at its rows times overlapping down tiles."""
     name = "moe_skewed"
     ws = _ws(name, 1024)
     ws.runs().zero_()
@@ -112,8 +113,9 @@ def test_event_invariants(sched, T):
     E, k, H, I = cfg["n_experts"], cfg["top_k"], cfg["hidden"], cfg["inter"]
     nr = min(128, 8192 // E, -(-T // 8))   # routing chunks of about 8 tokens
     rows, bn1, bn2 = moe_tiling(T, k)
-    tab = oev.moe_table(aux["counts"], rows, I, bn1, H, bn2, nr)
     ccols = 256 if -(-T // 16) * -(-H // 256) >= et.num_workers() else 64
+    tab = oev.moe_table(aux["counts"], rows, I, bn1, H, bn2, nr, tokens=T, top_k=k,
+                        comb_tok=16, comb_cols=ccols)
     ncomb = -(-T // 16) * -(-H // ccols)   # combine tiles of 16 tokens x ccols columns
     total = sum(tab["tasks"].values()) + ncomb
     runs = ws.runs().cpu().numpy()
@@ -121,8 +123,17 @@ def test_event_invariants(sched, T):
     cnt = ws.counters(1 - st["bank"]).cpu().numpy()
     assert cnt[0] == -nr                                   # all routing tasks notified
     ev_exp, ev_he, ev_h = 8, 8 + E, 8 + 2 * E
+    ev_c = ev_h + -(-1024 * k // 16) + E                   # after the block events (T_max 1024)
     nb = tab["blocks"]
-    assert cnt[4] == -(nb * (H // bn2))                    # all down tiles done
+    cg = tab["events"]["E_cg"]
+    ncg = int(np.prod(cg["shape"]))
+    if sched == "static" and T >= 256 and tab["tasks"]["down"] <= 4 * et.num_workers():
+        # shallow down phase: every combine tile waited on its own event
+        assert cnt[4] == 0
+        assert (cnt[ev_c:ev_c + ncg] == -cg["wait_count"].reshape(-1)).all()
+    else:
+        assert cnt[4] == -tab["tasks"]["down"]            # all down tiles done
+        assert (cnt[ev_c:ev_c + ncg] == 0).all()
     if sched == "dynamic":
         # data-dependent: rows per expert, and gate/up tiles over its blocks
         assert (cnt[ev_exp:ev_exp + E] == -tab["events"]["E_exp"]["wait_count"]).all()

@@ -111,6 +111,29 @@ def test_task_indptr_brute_force():
         assert tab["events"]["E_he"]["wait_count"].sum() == tab["tasks"]["gate_up"]
 
 
+def test_combine_group_events_brute_force():
+    """E_cg[g, c]: enumerate every (routed row, down tile, combine tile)
+    triple whose columns overlap and count the notifies per combine tile."""
+    rng = np.random.default_rng(3)
+    for T, k, H, dc, cc in ((37, 3, 512, 256, 64), (50, 2, 256, 16, 64), (16, 8, 768, 64, 256),
+                            (1, 1, 320, 64, 256)):
+        E = max(6, k + 1)
+        ids, _ = moe.route(rng.standard_normal((T, E)).astype(np.float32), k)
+        counts = np.bincount(ids.reshape(-1), minlength=E)
+        tab = events.moe_table(counts, 16, 64, 16, H, dc, 2, tokens=T, top_k=k, comb_tok=16,
+                               comb_cols=cc)
+        pairs = []
+        for t in range(T):
+            for s in range(k):
+                for n2 in range(H // dc):
+                    for c in range(-(-H // cc)):
+                        if n2 * dc < min(H, (c + 1) * cc) and c * cc < (n2 + 1) * dc:
+                            pairs.append(((t, s, n2), (t // 16, c)))
+        cg = events.notify_counts(pairs, tab["events"]["E_cg"]["shape"])
+        assert (tab["events"]["E_cg"]["wait_count"] == cg).all()
+        assert cg.sum() == T * k * (H // dc) * max(1, dc // cc)
+
+
 def _rand_experts(rng, E, H, I):
     return (rng.standard_normal((E, H, I)) * 0.3, rng.standard_normal((E, H, I)) * 0.3,
             rng.standard_normal((E, I, H)) * 0.3)
