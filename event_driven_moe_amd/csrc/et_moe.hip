@@ -505,6 +505,47 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   };
 
   // ------------------------------------------------------------- grouping
+  // Stable counting sort of the routed rows of tokens [ta, tb) (expert ids at
+  // ids[(t - ta) * k + s]): row (t, s) of expert e goes to position cur[e] +
+  // (rows of e among the range's earlier tokens).  The range is cut into S
+  // consecutive sub-ranges, one per 16-lane group: each counts its rows per
+  // expert, an exclusive prefix over the sub-ranges gives each its first
+  // position per expert, and each then places its own tokens in order (a
+  // token's k experts are distinct, so its lanes touch distinct cursors).
+  // cur[e] ends advanced by the range's rows of e.  cnt: S * E ints of LDS.
+  auto group_range = [&](int ta, int tb, const int* ids, int* cur, int* cnt, int S) ET_INLINE {
+    const int L = cdiv(tb - ta, S);
+    const int j = tid >> 4, l = tid & 15;
+    const int u0 = j * L, u1 = min(tb - ta, u0 + L);
+    const bool act = j < S && l < m.k;
+    for (int i = tid; i < S * m.E; i += kThreads) cnt[i] = 0;
+    __syncthreads();
+    if (act)
+      for (int u = u0; u < u1; ++u) atomicAdd(&cnt[j * m.E + ids[u * m.k + l]], 1);
+    __syncthreads();
+    for (int e = tid; e < m.E; e += kThreads) {
+      int run = cur[e];
+      for (int q = 0; q < S; ++q) {
+        const int v = cnt[q * m.E + e];
+        cnt[q * m.E + e] = run;
+        run += v;
+      }
+      cur[e] = run;
+    }
+    __syncthreads();
+    if (act)
+      for (int u = u0; u < u1; ++u) {
+        const int q = (ta + u) * m.k + l;
+        const int pos = cnt[j * m.E + ids[u * m.k + l]]++;
+        st_coh(&m.perm[pos], q);
+        st_coh(&m.inv[q], pos);
+      }
+    __syncthreads();
+  };
+
+  // Grouping task of routing chunk r: its rows start at the chunk bases the
+  // scan stored in hist[r, :]; the chunk's expert ids are staged in LDS, in
+  // passes of whole tokens when there are more than 2048 pairs.
   auto group = [&](int r) ET_INLINE {
     int* cur = s_i;            // [E] next position per expert
     int* base = s_i + 1024;    // [E] first position of this chunk per expert
@@ -513,55 +554,36 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       cur[e] = b;
       base[e] = b;
     }
-    __syncthreads();
+    int* ids = s_i + 3072;     // [2048]
+    int* cnt = s_i + 5120;     // [S * E] <= 3072
+    const int S = min(16, 3072 / m.E);
     const int t0 = r * m.tpr;
     const int t1 = min(m.T, t0 + m.tpr);
-    // the chunk's expert ids, loaded in parallel (chunks of up to 2048 pairs)
-    int* ids = s_i + 3072;
-    for (int q0 = t0 * m.k; q0 < t1 * m.k; q0 += 2048) {
-      const int q1 = min(t1 * m.k, q0 + 2048);
-      for (int q = q0 + tid; q < q1; q += kThreads) ids[q - q0] = ld_coh(&m.topk_ids[q]);
+    const int tp = 2048 / m.k;   // tokens per pass
+    for (int ta = t0; ta < t1; ta += tp) {
+      const int tb = min(t1, ta + tp);
+      for (int q = ta * m.k + tid; q < tb * m.k; q += kThreads) ids[q - ta * m.k] = ld_coh(&m.topk_ids[q]);
       __syncthreads();
-      if (wave == 0) {
-        for (int q = q0; q < q1; q += m.k) {   // tokens in order: stable positions
-          if (lane < m.k) {
-            const int e = ids[q - q0 + lane];
-            const int pos = cur[e]++;        // a token's k experts are distinct
-            st_coh(&m.perm[pos], q + lane);
-            st_coh(&m.inv[q + lane], pos);
-          }
-        }
-      }
-      __syncthreads();
+      group_range(ta, tb, ids, cur, cnt, S);
     }
   };
 
-  // Grouping of every chunk by the workgroup that just ran the scan: the
-  // scan left the per-(chunk, expert) offsets in LDS (hs, relative to the
-  // expert's first row tokp[e]); wave w takes chunks w, w + 4, ... and uses
-  // those offsets as its cursors.  The routed ids are staged in LDS first.
+  // Grouping of all T tokens by the workgroup that just ran the scan (T * k
+  // <= kInlinePairs): the rows start at the experts' first positions tokp[e];
+  // the routed ids are staged in LDS first (a solo routing chunk left them
+  // there already).
   auto group_inline = [&]() ET_INLINE {
-    int* hs = s_i;
     const int* tokp = reinterpret_cast<const int*>(s1);
     int* ids = reinterpret_cast<int*>(gen + kGenIdx);   // [T * k] (the index cache is not yet in use)
+    int* cur = s_i;                                      // [E]
+    int* cnt = s_i + kMaxExperts;                        // [S * E] <= kHistEntries - kMaxExperts
     cached = false;
     const int np = m.T * m.k;
-    if (!solo_route)   // a solo routing chunk left the chosen experts here already
+    if (!solo_route)
       for (int q = tid; q < np; q += kThreads) ids[q] = ld_coh(&m.topk_ids[q]);
+    for (int e = tid; e < m.E; e += kThreads) cur[e] = tokp[e];
     lds_barrier();
-    const int n_ne = cdiv(m.T, m.tpr);
-    for (int r = wave; r < n_ne; r += 4) {
-      const int t1 = min(m.T, (r + 1) * m.tpr);
-      for (int t = r * m.tpr; t < t1; ++t) {   // tokens in order: stable positions
-        if (lane < m.k) {
-          const int q = t * m.k + lane;
-          const int e = ids[q];
-          const int pos = tokp[e] + hs[r * m.E + e]++;   // a token's k experts are distinct
-          st_coh(&m.perm[pos], q);
-          st_coh(&m.inv[q], pos);
-        }
-      }
-    }
+    group_range(0, m.T, ids, cur, cnt, min(16, (kHistEntries - kMaxExperts) / m.E));
     lds_barrier();   // the caller releases before notifying
   };
 
