@@ -5,37 +5,36 @@
 // weighted combine at the end:
 //   routing task r   top-k of the router logits of token chunk r, renormalised
 //                    weights, a per-chunk expert histogram; notifies EV_ROUTE;
-//   scan task        column sums of the histograms (rows per expert), CSR
-//                    offsets of rows, row blocks and tasks per expert, and the
+//   scan             column sums of the histograms (rows per expert), CSR
+//                    offsets of rows, row blocks and tasks per expert, the
 //                    base position of every (chunk, expert); it learns the
 //                    number of GEMM tasks of this call;
-//   grouping task r  stable positions of chunk r's (token, slot) pairs; notifies
-//                    EV_EXP[e] of the experts its tokens chose, by its number of
-//                    rows for each (data-dependent targets, data-dependent wait
-//                    count = rows routed to e);
-//   gate/up task     (block gb, 16 columns of h): rows gathered from x by the
-//                    permutation; h = SiLU(x Wg) * (x Wu) in bf16; notifies
-//                    EV_H[gb];
-//   down task        (block gb, 16 output columns): y = h Wd in fp32; waits on
-//                    EV_H[gb] only, not on all gate/up tasks -- the event that
-//                    removes the barrier between the two GroupGEMMs;
-//   combine          out[t] = sum_s w[t, s] y[inv[t, s]] in slot order.
-// Static and dynamic modes run the scan inline in the routing task whose
-// notify completes EV_ROUTE (the notify that fires an event runs its single
-// consumer, with no queue slot or wait), and when few pairs were routed
-// (T * k <= kInlinePairs) the same workgroup also groups all chunks right
-// after the scan.  The barrier and per-operator baselines keep them as tasks
-// of their own.
-// Dynamic mode: the notify that zeroes EV_EXP[e] pushes expert e's task range
-// tasks[task_indptr[e] : task_indptr[e+1]] (data-dependent fan-out), the one
-// that zeroes EV_H[gb] pushes block gb's down tasks, and the one that zeroes
-// EV_C[t, c] (k down rows of token t for column tile c) runs that combine
-// inline -- in static mode too: EV_C's wait count (k) and index are known
-// statically, only its producers depend on the routing.  Static mode keeps
-// the fine-grained EV_H edge but, as the page's static lowering does for
-// data-dependent edges, replaces EV_EXP by one coarse "all grouped" event.
-// The barrier baseline uses one event per operator throughout, with the
-// combine as tiles of its own after an "all down tiles done" event.
+//   grouping r       stable positions of chunk r's (token, slot) pairs;
+//                    dynamic: notifies EV_EXP[e] of the experts its tokens
+//                    chose, by its number of rows for each (data-dependent
+//                    targets, data-dependent wait count = rows routed to e);
+//   gate/up task     (block gb, bn1 columns of h): rows gathered from x by the
+//                    permutation; h = SiLU(x Wg) * (x Wu) in bf16; static:
+//                    notifies EV_H[gb]; dynamic: EV_HE[e] (all of expert e's
+//                    gate/up tiles);
+//   down task        (block gb, bn2 output columns): y = h Wd (bf16 rows);
+//                    waits on EV_H[gb] only, not on all gate/up tasks -- the
+//                    event that removes the barrier between the two
+//                    GroupGEMMs (dynamic: pushed when EV_HE[e] fires);
+//   combine          out[t] = sum_s w[t, s] y[inv[t, s]] in slot order, in
+//                    tiles after EV_DOWN (all down tiles), after EV_CG[group,
+//                    column tile] (static, shallow down phases), or inline in
+//                    the down tile completing EV_C[t, c] (a few tokens).
+// Static and dynamic modes: every routing workgroup, once all histograms are
+// out (EV_ROUTE), runs its own share of the scan (the totals, and the rows
+// of earlier chunks for its own chunk) and groups its own chunk, so neither
+// the scan nor the grouping is a task of its own or a hop through an event.
+// Dynamic: the grouping that completes EV_EXP[e] pushes expert e's task range
+// tasks[task_indptr[e] : task_indptr[e+1]] (data-dependent fan-out).  Static
+// mode keeps the fine-grained EV_H edge but, as the page's static lowering
+// does for data-dependent edges, replaces EV_EXP by one coarse "all grouped"
+// event.  The barrier and per-operator baselines keep the scan and the
+// grouping as tasks of their own and use one event per operator throughout.
 #include <type_traits>
 
 #include "et_device.hpp"
@@ -71,7 +70,9 @@ struct MoeArgs {
 // LDS: three slot arrays (the GEMM ring of the wide variants; scratch for
 // the other task kinds) and a small general region.
 constexpr int kScanHistBytes = kHistEntries * 4;                    // slot 0
-constexpr int kScanTempBytes = (2 * kMaxExperts + 8 + kThreads) * 4; // slot 1
+// slot 1 during the scan: counts, blocks, 8 scan temporaries, partial sums;
+// the per-chunk scan adds rows-before-chunk and their partial sums
+constexpr int kScanTempBytes = (3 * kMaxExperts + 8 + 2 * kThreads) * 4;
 constexpr int kGenRowsOff = 0, kGenFired = 512, kGenIdx = 1024;
 // Static and dynamic schedules with at most this many tokens: the combine
 // runs inline in the down tile whose notify completes a token's k rows for
@@ -181,13 +182,17 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   const int nt1 = m.I / bn1, nt2 = m.H / bn2;
   const int NR = m.NR;
   const int base1 = 2 * NR + 1;
-  // static / dynamic with few routed pairs: grouping runs inline after the scan
-  const bool inline_group = (sched == ET_SCHED_STATIC || sched == ET_SCHED_DYNAMIC) &&
-                            m.T * m.k <= kInlinePairs;
-  // one routing chunk (static / dynamic): its workgroup runs the scan and the
-  // grouping right after it, so the histogram and the chosen experts stay in
-  // LDS and no global round trip or store-completion wait separates them
-  const bool solo_route = NR == 1 && inline_group;
+  // static / dynamic: every routing workgroup also scans and groups its own
+  // chunk (no scan or grouping tasks of their own)
+  const bool fused_front = sched == ET_SCHED_STATIC || sched == ET_SCHED_DYNAMIC;
+  // one routing chunk (static / dynamic): the histogram and the chosen
+  // experts stay in LDS, and no global round trip separates routing from
+  // the scan and the grouping
+  const bool solo_route = NR == 1 && fused_front;
+  // static / dynamic: the routing workgroup keeps its chunk's expert ids in
+  // LDS for its own grouping when they fit (the index cache's space, unused
+  // until the gemm tasks)
+  const bool keep_ids = fused_front && m.tpr * m.k <= kIdxCache / 4;
   const int wc = m.k;   // EV_C wait count: the k rows of a token, one per down column tile
   // (compiled into the 16-row variant only, the one tiny token counts use:
   // the extra path measurably slowed the other variants' down tiles)
@@ -325,7 +330,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   // -0.0 and +0.0 share a key), with two DPP reductions and no LDS traffic.
   auto route = [&](int r) ET_INLINE {
     int* hist_l = s_i;   // [E]
-    int* ids_l = reinterpret_cast<int*>(gen + kGenIdx);   // [T * k] when solo_route
+    int* ids_l = reinterpret_cast<int*>(gen + kGenIdx);   // [tpr * k] when keep_ids
     for (int e = tid; e < m.E; e += kThreads) hist_l[e] = 0;
     __syncthreads();
     const int t0 = r * m.tpr;
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
             st_coh(&m.topk_ids[t * m.k + lane], my_e[b]);
             st_coh(&m.topk_w[t * m.k + lane], ex / sum);
             atomicAdd(&hist_l[my_e[b]], 1);
-            if (solo_route) ids_l[t * m.k + lane] = my_e[b];
+            if (keep_ids) ids_l[(t - t0) * m.k + lane] = my_e[b];
           }
         }
       }
@@ -514,6 +519,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   // token's k experts are distinct, so its lanes touch distinct cursors).
   // cur[e] ends advanced by the range's rows of e.  cnt: S * E ints of LDS.
   auto group_range = [&](int ta, int tb, const int* ids, int* cur, int* cnt, int S) ET_INLINE {
+    S = min(S, max(1, cdiv(tb - ta, 4)));   // sub-ranges of >= 4 tokens: S prefix steps vs n / S placements
     const int L = cdiv(tb - ta, S);
     const int j = tid >> 4, l = tid & 15;
     const int u0 = j * L, u1 = min(tb - ta, u0 + L);
@@ -543,22 +549,22 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     __syncthreads();
   };
 
-  // Grouping task of routing chunk r: its rows start at the chunk bases the
-  // scan stored in hist[r, :]; the chunk's expert ids are staged in LDS, in
-  // passes of whole tokens when there are more than 2048 pairs.
-  auto group = [&](int r) ET_INLINE {
-    int* cur = s_i;            // [E] next position per expert
-    int* base = s_i + 1024;    // [E] first position of this chunk per expert
-    for (int e = tid; e < m.E; e += kThreads) {
-      const int b = ld_coh(&m.hist[r * m.E + e]);
-      cur[e] = b;
-      base[e] = b;
-    }
-    int* ids = s_i + 3072;     // [2048]
+  // Grouping of routing chunk r with the cursors (first position of the
+  // chunk's rows per expert) in s_i[0, E): the chunk's expert ids are staged
+  // in LDS in passes of whole tokens (at most 2048 pairs), unless the routing
+  // workgroup left them there (keep_ids).
+  auto group_chunk = [&](int r) ET_INLINE {
+    int* cur = s_i;            // [E]
     int* cnt = s_i + 5120;     // [S * E] <= 3072
     const int S = min(16, 3072 / m.E);
     const int t0 = r * m.tpr;
     const int t1 = min(m.T, t0 + m.tpr);
+    if (keep_ids) {
+      group_range(t0, t1, reinterpret_cast<const int*>(gen + kGenIdx), cur, cnt, S);
+      cached = false;          // the ids sat in the index cache's space
+      return;
+    }
+    int* ids = s_i + 3072;     // [2048]
     const int tp = 2048 / m.k;   // tokens per pass
     for (int ta = t0; ta < t1; ta += tp) {
       const int tb = min(t1, ta + tp);
@@ -568,23 +574,102 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     }
   };
 
-  // Grouping of all T tokens by the workgroup that just ran the scan (T * k
-  // <= kInlinePairs): the rows start at the experts' first positions tokp[e];
-  // the routed ids are staged in LDS first (a solo routing chunk left them
-  // there already).
-  auto group_inline = [&]() ET_INLINE {
-    const int* tokp = reinterpret_cast<const int*>(s1);
-    int* ids = reinterpret_cast<int*>(gen + kGenIdx);   // [T * k] (the index cache is not yet in use)
-    int* cur = s_i;                                      // [E]
-    int* cnt = s_i + kMaxExperts;                        // [S * E] <= kHistEntries - kMaxExperts
-    cached = false;
-    const int np = m.T * m.k;
-    if (!solo_route)
-      for (int q = tid; q < np; q += kThreads) ids[q] = ld_coh(&m.topk_ids[q]);
-    for (int e = tid; e < m.E; e += kThreads) cur[e] = tokp[e];
+  // Grouping task of routing chunk r (barrier and per-op schedules): its rows
+  // start at the chunk bases the scan stored in hist[r, :].
+  auto group = [&](int r) ET_INLINE {
+    for (int e = tid; e < m.E; e += kThreads) {
+      const int b = ld_coh(&m.hist[r * m.E + e]);
+      s_i[e] = b;
+      s_i[1024 + e] = b;
+    }
+    group_chunk(r);
+  };
+
+  // ------------------------------------------------------------- chunk scan
+  // Static and dynamic schedules: once every chunk's histogram is published
+  // (EV_ROUTE), routing workgroup r computes what its grouping needs itself
+  // instead of waiting for one scan task: per expert the rows over all
+  // chunks and the rows in chunks before r, then the experts' first rows
+  // (tok_indptr) and first blocks (blk_indptr).  Every routing workgroup
+  // stores the same indptr arrays and task totals (identical values), so
+  // one that releases or pushes gemm tasks has published what they read
+  // itself.  Leaves the cursors of chunk r in s_i[0, E) and a copy in
+  // s_i[1024, 1024 + E), the exclusive tok_indptr / blk_indptr in s1[0, E) /
+  // s1[1024, 1024 + E).  Returns the number of row blocks.
+  auto scan_chunk = [&](int r) ET_INLINE -> int {
+    int* hs = s_i;                         // [n_ne][E]
+    int* cnt = reinterpret_cast<int*>(s1); // [E]
+    int* blk = cnt + 1024;                 // [E]
+    int* tmp = blk + 1024;                 // [8]
+    int* part = tmp + 8;                   // [256]
+    int* bef = part + kThreads;            // [E] rows in chunks before r
+    int* partb = bef + kMaxExperts;        // [256]
+    const int n_ne = cdiv(m.T, m.tpr);
+    const int tot = n_ne * m.E;
+    if (!solo_route) {   // a solo chunk's histogram is in hs already
+      const Rsrc rhist = make_rsrc(m.hist, (uint32_t)(4 * tot + 15) & ~15u);
+      for (int ch = wave; ch < cdiv(tot, 256); ch += 4)
+        dma16<true>(rhist, hs + 256 * ch, (uint32_t)(1024 * ch + 16 * lane));
+      wait_mem();
+    }
+    __syncthreads();
+    // P threads per expert sum about n_ne / P chunks each (all rows, and the
+    // rows of chunks before r), then the P partial sums are added
+    int P = m.E >= kThreads ? 1 : kThreads / m.E;
+    P = min(P, cdiv(n_ne, 4));
+    const int span = cdiv(n_ne, P);
+    for (int q = tid; q < m.E * P; q += kThreads) {
+      const int e = q / P, p = q % P;
+      int a_all = 0, a_bef = 0;
+#pragma unroll 8
+      for (int rr = p * span; rr < min(n_ne, (p + 1) * span); ++rr) {
+        const int v = hs[rr * m.E + e];
+        a_all += v;
+        a_bef += rr < r ? v : 0;
+      }
+      if (P == 1) {
+        cnt[e] = a_all;
+        bef[e] = a_bef;
+      } else {
+        part[q] = a_all;
+        partb[q] = a_bef;
+      }
+    }
+    __syncthreads();
+    if (P > 1)
+      for (int e = tid; e < m.E; e += kThreads) {
+        int a_all = 0, a_bef = 0;
+        for (int p = 0; p < P; ++p) {
+          a_all += part[e * P + p];
+          a_bef += partb[e * P + p];
+        }
+        cnt[e] = a_all;
+        bef[e] = a_bef;
+      }
+    __syncthreads();
+    for (int e = tid; e < m.E; e += kThreads) {
+      blk[e] = cdiv(cnt[e], rows);
+      st_coh(&m.counts[e], cnt[e]);
+    }
     lds_barrier();
-    group_range(0, m.T, ids, cur, cnt, min(16, (kHistEntries - kMaxExperts) / m.E));
-    lds_barrier();   // the caller releases before notifying
+    block_exscan(cnt, m.E, tmp);           // cnt -> tok_indptr
+    const int nb = block_exscan(blk, m.E, tmp);
+    for (int e = tid; e < m.E; e += kThreads) {
+      st_coh(&m.tok_indptr[e], cnt[e]);
+      st_coh(&m.blk_indptr[e], blk[e]);
+      st_coh(&m.task_indptr[e], blk[e] * nt1);
+      s_i[e] = s_i[1024 + e] = cnt[e] + bef[e];   // hs is no longer read
+    }
+    if (tid == 0) {
+      st_coh(&m.tok_indptr[m.E], m.T * m.k);
+      st_coh(&m.blk_indptr[m.E], nb);
+      st_coh(&m.task_indptr[m.E], nb * nt1);
+      st_rlx(&ra.hdr[HDR_META + MD_NB], nb);
+      st_rlx(&ra.hdr[HDR_META + MD_TOTAL1], nb * nt1);
+      st_rlx(&ra.hdr[HDR_META + MD_TOTAL2], nb * nt2);
+    }
+    lds_barrier();
+    return nb;
   };
 
   // ------------------------------------------------------------- gemm tiles
@@ -871,80 +956,84 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     if (task < NR) {
       route(task);
       if (sched == ET_SCHED_PER_OP) return true;
-      if (solo_route) {
-        // EV_ROUTE's only consumer is this workgroup's scan, which reads LDS
-        t0_notify(c, EV_ROUTE, 1, NR, task);
-      } else {
+      if (sched == ET_SCHED_BARRIER) {
         wg_release();
-        if (sched == ET_SCHED_BARRIER) {
-          t0_notify(c, EV_ROUTE, 1, NR, task);
-          return true;
-        }
-        if (!wg_notify(c, EV_ROUTE, 1, NR, task)) return true;
+        t0_notify(c, EV_ROUTE, 1, NR, task);
+        return true;
       }
-      // this notify completed EV_ROUTE: the scan runs here
+      // static / dynamic: once every chunk's histogram is out, this
+      // workgroup scans and groups its own chunk
+      if (!solo_route) {
+        wg_release();
+        t0_notify(c, EV_ROUTE, 1, NR, task);
+        if (!wg_wait(c, EV_ROUTE, NR, task)) return false;
+      } else {
+        t0_notify(c, EV_ROUTE, 1, NR, task);
+      }
       long long ts = trace_now(c);
-      const int nb = scan();
-      count_run(c, NR);
-      trace_task(c, NR, ts);
-      if (!inline_group) {
-        if (sched == ET_SCHED_DYNAMIC) {
-          set_total(c, 2 * NR + nb * (nt1 + nt2) + ncomb);
-          wg_release();
-          wg_push(c, NR, [&](int i) { return NR + 1 + i; },    // the grouping tasks
-                  [&](int i) { return i; });
-        } else {
+      const int nb = scan_chunk(task);
+      if (task == 0) {
+        count_run(c, NR);
+        trace_task(c, NR, ts);
+        if (sched == ET_SCHED_STATIC) {   // task totals are out: gemm tasks may start and prefetch weights
           wg_release();
           t0_notify(c, EV_SCAN, 1, 1, NR);
         }
-        return true;
-      }
-      if (sched == ET_SCHED_STATIC) {   // tasks may start and prefetch weights while grouping runs
-        wg_release();
-        t0_notify(c, EV_SCAN, 1, 1, NR);
       }
       ts = trace_now(c);
-      group_inline();
-      for (int r = 0; r < NR; ++r) {
-        count_run(c, NR + 1 + r);
-        trace_task(c, NR + 1 + r, ts);
-      }
+      group_chunk(task);
+      count_run(c, NR + 1 + task);
+      trace_task(c, NR + 1 + task, ts);
       wg_release();
       if (sched == ET_SCHED_STATIC) {
-        t0_notify(c, EV_GROUP, NR, NR, NR + 1);
+        t0_notify(c, EV_GROUP, 1, NR, task);
         return true;
       }
-      // dynamic: every expert event receives all of its rows at once (its
-      // data-dependent wait count) and fires; the fired experts' task ranges
-      // together are the whole gate/up range, pushed in one piece
+      // dynamic: data-dependent notify targets -- the experts this chunk's
+      // tokens chose, each decremented by this chunk's rows for it; the
+      // experts whose events this completes have all their gate/up tiles
+      // pushed in one piece (block-major within each expert)
       set_total(c, NR + nb * (nt1 + nt2) + ncomb);
+      const int* cur = s_i;
+      const int* base = s_i + 1024;
+      int* fe = s_i + 2048;     // fired experts
+      int* fpre = s_i + 3072;   // their gate/up task counts -> exclusive prefix
+      const int* tokp = reinterpret_cast<const int*>(s1);
+      const int* blk = tokp + 1024;
+      if (tid == 0) sh.v[6] = 0;
+      __syncthreads();
       for (int e = tid; e < m.E; e += kThreads) {
-        const int n = ld_coh(&m.counts[e]);
+        const int n = cur[e] - base[e];
         if (n > 0) {
+          const int wcnt = (e + 1 < m.E ? tokp[e + 1] : m.T * m.k) - tokp[e];
           const int old = add_rlx(c.ev + m.ev_exp + e, -n);
-          if (old != 0) raise_fault(ra, ET_ESTATE, NR + 1, m.ev_exp + e, old - n);
+          if (old - n == -wcnt) fe[atomicAdd(&sh.v[6], 1)] = e;
+          else if (old - n < -wcnt) raise_fault(ra, ET_ESTATE, task, m.ev_exp + e, old - n);
         }
       }
-      // key of gate/up task i: its weight tile (expert, column tile); the
-      // scan's block offsets per expert are still in LDS
-      const int* blk = reinterpret_cast<const int*>(s1) + 1024;
-      auto expert_of = [&](int i) ET_INLINE {
-        int lo = 0, hi = m.E;
+      __syncthreads();
+      const int nf = sh.v[6];
+      if (nf == 0) return true;
+      auto nblk_of = [&](int e) ET_INLINE { return (e + 1 < m.E ? blk[e + 1] : nb) - blk[e]; };
+      for (int i = tid; i < nf; i += kThreads) fpre[i] = nblk_of(fe[i]) * nt1;
+      __syncthreads();
+      const int ntask = block_exscan(fpre, nf, reinterpret_cast<int*>(s1) + 2048);
+      auto slot_of = [&](int i) ET_INLINE {   // fired expert holding task i
+        int lo = 0, hi = nf;
         while (hi - lo > 1) {
           const int mid = (lo + hi) >> 1;
-          if (blk[mid] * nt1 <= i) lo = mid; else hi = mid;
+          if (fpre[mid] <= i) lo = mid; else hi = mid;
         }
         return lo;
       };
-      wg_push(c, nb * nt1,
-              [&](int i) {   // block-major within the expert's range
-                const int e = expert_of(i), l = i - blk[e] * nt1;
-                const int nblk = (e + 1 < m.E ? blk[e + 1] : nb) - blk[e];
-                return base1 + blk[e] * nt1 + (l % nt1) * nblk + l / nt1;
-              },
+      wg_push(c, ntask,
               [&](int i) {
-                const int e = expert_of(i);
-                return e * nt1 + (i - blk[e] * nt1) % nt1;
+                const int j = slot_of(i), e = fe[j], l = i - fpre[j];
+                return base1 + blk[e] * nt1 + (l % nt1) * nblk_of(e) + l / nt1;
+              },
+              [&](int i) {   // key: the weight tile (expert, column tile)
+                const int j = slot_of(i);
+                return fe[j] * nt1 + (i - fpre[j]) % nt1;
               });
       return true;
     }
@@ -956,43 +1045,13 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       t0_notify(c, EV_SCAN, 1, 1, task);
       return true;
     }
-    if (task < base1) {
+    if (task < base1) {   // grouping tasks: barrier and per-op modes
       const int r = task - NR - 1;
-      if (sched == ET_SCHED_STATIC || sched == ET_SCHED_BARRIER)
-        if (!wg_wait(c, EV_SCAN, 1, task)) return false;
+      if (sched == ET_SCHED_BARRIER && !wg_wait(c, EV_SCAN, 1, task)) return false;
       group(r);
       if (sched == ET_SCHED_PER_OP) return true;
       wg_release();
-      if (sched != ET_SCHED_DYNAMIC) {
-        t0_notify(c, EV_GROUP, 1, NR, task);
-        return true;
-      }
-      // dynamic: data-dependent notify targets -- the experts this chunk's
-      // tokens chose, each decremented by this chunk's rows for it
-      int* base = s_i + 1024;
-      int* cur = s_i;
-      int* fe = s_i + 2048;   // fired experts
-      if (tid == 0) sh.v[6] = 0;
-      __syncthreads();
-      for (int e = tid; e < m.E; e += kThreads) {
-        const int n = cur[e] - base[e];
-        if (n > 0) {
-          const int wcnt = ld_coh(&m.counts[e]);
-          const int old = add_rlx(c.ev + m.ev_exp + e, -n);
-          if (old - n == -wcnt) fe[atomicAdd(&sh.v[6], 1)] = e;
-          else if (old - n < -wcnt) raise_fault(ra, ET_ESTATE, task, m.ev_exp + e, old - n);
-        }
-      }
-      __syncthreads();
-      const int nf = sh.v[6];
-      for (int i = 0; i < nf; ++i) {
-        const int e = fe[i];
-        const int lo = ld_coh(&m.task_indptr[e]), hi = ld_coh(&m.task_indptr[e + 1]);
-        const int nblk = (hi - lo) / nt1;
-        wg_push(c, hi - lo, [&](int j) { return base1 + lo + (j % nt1) * nblk + j / nt1; },
-                [&](int j) { return e * nt1 + j % nt1; });   // key: (expert, column tile)
-      }
-      __syncthreads();
+      t0_notify(c, EV_GROUP, 1, NR, task);
       return true;
     }
     const int total1 = meta(MD_TOTAL1), total2 = meta(MD_TOTAL2);
@@ -1042,7 +1101,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       if (ok) count_run(c, NR);
       if (ok) trace_task(c, NR, t0);
     }
-    for (int r = c.wg; ok && !inline_group && r < NR; r += c.G) {
+    for (int r = c.wg; ok && sched == ET_SCHED_BARRIER && r < NR; r += c.G) {
       const long long t0 = trace_now(c);
       ok = run(NR + 1 + r);
       if (ok) count_run(c, NR + 1 + r);

@@ -142,7 +142,6 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kHistEntries = 8192;    // n_route * E must fit (int32, 32 KB of LDS)
 constexpr int kRouteTok = 8;          // tokens per routing chunk (fewer chunks when T is small)
-constexpr int kInlinePairs = 2048;    // T * k up to this: grouping runs inline after the scan
 
 enum : int { EV_ROUTE = 0, EV_SCAN = 1, EV_GROUP = 2, EV_G1ALL = 3, EV_DOWN = 4, EV_FIXED = 8 };
 
