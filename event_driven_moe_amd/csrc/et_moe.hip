@@ -212,6 +212,18 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     return sched == ET_SCHED_STATIC && !inline_comb && cdiv(m.T, kCombTok) >= kCombGroupMin &&
            total2 <= kCombGroupRounds * c.G;
   };
+  // Dynamic: queue shard key of gate/up or down tile (expert e, column tile n
+  // of nt).  The wide variants with 16 or more column tiles per expert key
+  // groups of 4 adjacent tiles together: a shard then holds, block by block,
+  // the same 4 weight tiles, so a batched claim takes one block's A rows
+  // through 4 tiles and the workers beside it stream the same tiles for the
+  // next blocks (moe_large T=8192 dynamic 8.78-8.82 -> 8.27-8.30 ms, T=2048
+  // 4.17-4.18 -> 4.01-4.02 ms).  With fewer tiles (moe_skewed: 6 and 8) the
+  // groups would leave shards short of work, so each tile keys alone.
+  auto tile_key = [&](int e, int n, int nt) ET_INLINE {
+    const int g = (kWide && nt >= 16) ? 4 : 1;
+    return e * cdiv(nt, g) + n / g;
+  };
   // wait count of E_cg[tc, cc]: k rows per token of the group, times the down
   // column tiles overlapping the combine tile's columns
   auto comb_wait = [&](int tc, int cc) ET_INLINE {
@@ -785,7 +797,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
         // claims taken beside it stream the same tiles for the next blocks
         const int b2 = base1 + meta(MD_TOTAL1) + c_blk[e] * nt2;
         wg_push(c, nblk * nt2, [&](int i) { return b2 + (i % nt2) * nblk + i / nt2; },
-                [&](int i) { return e * nt2 + i % nt2; });   // key: the weight tile (e, column tile)
+                [&](int i) { return tile_key(e, i % nt2, nt2); });
       }
     }
     return true;
@@ -1031,9 +1043,9 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
                 const int j = slot_of(i), e = fe[j], l = i - fpre[j];
                 return base1 + blk[e] * nt1 + (l % nt1) * nblk_of(e) + l / nt1;
               },
-              [&](int i) {   // key: the weight tile (expert, column tile)
+              [&](int i) {
                 const int j = slot_of(i);
-                return fe[j] * nt1 + (i - fpre[j]) % nt1;
+                return tile_key(fe[j], (i - fpre[j]) % nt1, nt1);
               });
       return true;
     }
