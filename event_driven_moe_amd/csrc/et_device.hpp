@@ -96,6 +96,7 @@ struct Shared {
 struct Ctx {
   RunArgs a;
   int* ev;             // this call's bank
+  int gen;             // this call's generation (completed calls + 1): broadcast flag value
   int wg, G;
   Shared* sh;
 };
@@ -237,6 +238,63 @@ __device__ __forceinline__ void t0_notify(const Ctx& c, int idx, int n, int wait
   (void)task;
   if (threadIdx.x == 0)
     __hip_atomic_fetch_add(c.ev + idx, -n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Broadcast events.  A coarse event that many workgroups wait on (every
+// routing chunk, the scan, every grouping chunk, every gate/up or down tile)
+// is not polled on its counter: the notify that completes the counter writes
+// this call's generation into the kBcastLines flag lines of the event's slot,
+// and each waiter polls the line of its own workgroup (wg mod kBcastLines).
+// With all waiters polling one counter, their loads queued at one address and
+// a waiter saw the event 2-4 us after it fired.  The flags need no arming:
+// a line holds the generation of the last call that fired its event, and
+// the generation grows with every call (the epilogue counts the calls).  The
+// counter is still decremented, so its final value is checked as for any
+// other event.  Every notify of such an event must use t0_notify_bcast.
+__device__ __forceinline__ int* bcast_line(const Ctx& c, int slot, int line) {
+  return c.a.hdr + HDR_FLAGS + (slot * kBcastLines + line) * 32;
+}
+
+// Whole workgroup, after wg_release(): wave 0 notifies; when its decrement
+// completes the event, its 64 lanes write the 64 flag lines.
+__device__ __forceinline__ void t0_notify_bcast(const Ctx& c, int idx, int slot, int n,
+                                                int wait_count, int task) {
+  static_assert(kBcastLines == 64, "one flag line per lane of wave 0");
+  if (threadIdx.x < 64) {
+    int old = 0;
+    if (threadIdx.x == 0) old = add_rlx(c.ev + idx, -n);
+    const int now = __builtin_amdgcn_readfirstlane(old) - n;
+    if (now == -wait_count)
+      st_rlx(bcast_line(c, slot, threadIdx.x), c.gen);
+    else if (now < -wait_count && threadIdx.x == 0)
+      raise_fault(c.a, ET_ESTATE, task, idx, now);
+  }
+}
+
+// Thread 0 polls its workgroup's flag line of `slot` until it holds this
+// call's generation.  Returns 1, or 0 after a fault or the watchdog.
+__device__ __forceinline__ int spin_flag(const Ctx& c, int idx, int slot, int task) {
+  const int* p = bcast_line(c, slot, c.wg % kBcastLines);
+  if (ld_rlx(p) == c.gen) return 1;
+  const long long t0 = now_ticks();
+  for (int it = 1;; ++it) {
+    __builtin_amdgcn_s_sleep(1);
+    if (ld_rlx(p) == c.gen) return 1;
+    if ((it & 63) == 0) {
+      if (faulted(c.a)) return 0;
+      if (now_ticks() - t0 > c.a.timeout) {
+        raise_fault(c.a, ET_ETIMEOUT, task, idx, ld_rlx(c.ev + idx));
+        return 0;
+      }
+    }
+  }
+}
+
+// wait() on a broadcast event: the whole workgroup holds until it fired.
+__device__ __forceinline__ bool wg_wait_bcast(const Ctx& c, int idx, int slot, int task) {
+  int ok = 1;
+  if (threadIdx.x == 0) ok = spin_flag(c, idx, slot, task);
+  return wg_bcast(c, ok, 1) != 0;
 }
 
 __device__ __forceinline__ int* q_claimed(const RunArgs& a, int q) { return a.qctl + q * kQCtlStride; }
@@ -429,13 +487,21 @@ __device__ __forceinline__ bool prologue(Ctx& c, const RunArgs& a, Shared* sh) {
   c.sh = sh;
   c.wg = blockIdx.x;
   c.G = gridDim.x;
-  if (ld_rlx(&a.hdr[HDR_ERR]) != 0) return false;
-  int bank = ld_rlx(&a.hdr[HDR_BANK]) & 1;
-  c.ev = a.counters + (size_t)bank * a.n_events;
   trace_wg(c, 0);
+  // the four header words are requested together (one memory round trip,
+  // not three dependent ones)
+  const int err = ld_rlx(&a.hdr[HDR_ERR]);
+  const int bank_w = ld_rlx(&a.hdr[HDR_BANK]);
+  const int ext0 = ld_rlx(&a.hdr[HDR_EXT0]);
+  const int ext1 = ld_rlx(&a.hdr[HDR_EXT1]);
+  const int calls = ld_rlx(&a.hdr[HDR_CALLS]);
+  if (err != 0) return false;
+  c.gen = calls + 1;
+  const int bank = bank_w & 1;
+  c.ev = a.counters + (size_t)bank * a.n_events;
   if (a.sched != ET_SCHED_PER_OP) {
     int* other = a.counters + (size_t)(1 - bank) * a.n_events;
-    int ext = ld_rlx(&a.hdr[HDR_EXT0 + (1 - bank)]);
+    int ext = bank ? ext0 : ext1;
     if (ext > a.n_events) ext = a.n_events;
     for (int i = c.wg * kThreads + threadIdx.x; i < ext; i += c.G * kThreads) other[i] = 0;
   }

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kThreads, kMlpOcc<MT>) void mlp_kernel(RunArgs ra, 
       if (sched == ET_SCHED_PER_OP) return true;
       wg_release();
       if (sched == ET_SCHED_BARRIER)
-        t0_notify(c, m.ev_all, 1, n_gate, task);
+        t0_notify_bcast(c, m.ev_all, 0, 1, n_gate, task);
       else
         t0_notify(c, b * nht + n / (kHTile / 16), 1, kHTile / 16, task);
       return true;
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kThreads, kMlpOcc<MT>) void mlp_kernel(RunArgs ra, 
     bool ready = sched == ET_SCHED_PER_OP;
     auto gate = [&](int round) ET_INLINE -> bool {
       if (ready) return true;
-      if (sched == ET_SCHED_BARRIER) return round > 0 || wg_wait(c, m.ev_all, n_gate, task);
+      if (sched == ET_SCHED_BARRIER) return round > 0 || wg_wait_bcast(c, m.ev_all, 0, task);
       // one round trip checks every h tile of the row block; if some are not
       // done yet, wait only for the K-blocks of the coming round
       if (round == 0 && wg_probe_range(c, b * nht, nht, kHTile / 16)) {

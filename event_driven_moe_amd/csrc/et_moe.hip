@@ -189,6 +189,12 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   // experts stay in LDS, and no global round trip separates routing from
   // the scan and the grouping
   const bool solo_route = NR == 1 && fused_front;
+  // With at least kBcastChunks routing chunks, the events their workgroups
+  // wait on (EV_ROUTE; dynamic: EV_SCAN before pushing) are broadcast events
+  // and chunk 0 alone publishes the scan results; with fewer, polling the
+  // counter is not contended, every chunk publishes the same scan results,
+  // and a chunk needs no second event before it pushes.
+  const bool many_chunks = NR >= kBcastChunks;
   // static / dynamic: the routing workgroup keeps its chunk's expert ids in
   // LDS for its own grouping when they fit (the index cache's space, unused
   // until the gemm tasks)
@@ -340,6 +346,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   // experts l, l + 64, ...; each of the k rounds takes the wave-wide largest
   // key, then the lowest expert index holding it (ties go to the lower index;
   // -0.0 and +0.0 share a key), with two DPP reductions and no LDS traffic.
+
   auto route = [&](int r) ET_INLINE {
     int* hist_l = s_i;   // [E]
     int* ids_l = reinterpret_cast<int*>(gen + kGenIdx);   // [tpr * k] when keep_ids
@@ -602,10 +609,10 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   // (EV_ROUTE), routing workgroup r computes what its grouping needs itself
   // instead of waiting for one scan task: per expert the rows over all
   // chunks and the rows in chunks before r, then the experts' first rows
-  // (tok_indptr) and first blocks (blk_indptr).  Every routing workgroup
-  // stores the same indptr arrays and task totals (identical values), so
-  // one that releases or pushes gemm tasks has published what they read
-  // itself.  Leaves the cursors of chunk r in s_i[0, E) and a copy in
+  // (tok_indptr) and first blocks (blk_indptr).  Chunk 0 stores them and
+  // the task totals for the gemm tasks and fires EV_SCAN; a workgroup that
+  // pushes gemm tasks first sees EV_SCAN fired, so what the tasks read is
+  // published before they can be claimed.  Leaves the cursors of chunk r in s_i[0, E) and a copy in
   // s_i[1024, 1024 + E), the exclusive tok_indptr / blk_indptr in s1[0, E) /
   // s1[1024, 1024 + E).  Returns the number of row blocks.
   auto scan_chunk = [&](int r) ET_INLINE -> int {
@@ -659,20 +666,29 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
         bef[e] = a_bef;
       }
     __syncthreads();
+    // Chunk 0 publishes the scan results (counts, the CSR offsets and the
+    // task totals) and then fires EV_SCAN; the other chunks keep them in LDS
+    // (dynamic, few chunks: every chunk publishes them).  When all 64 chunks
+    // stored the same values, their stores to the same lines queued behind
+    // each other and chunk 0 spent 6.5 us completing its own (moe_skewed
+    // T=1024).
+    const bool pub = r == 0 || (sched == ET_SCHED_DYNAMIC && !many_chunks);
     for (int e = tid; e < m.E; e += kThreads) {
       blk[e] = cdiv(cnt[e], rows);
-      st_coh(&m.counts[e], cnt[e]);
+      if (pub) st_coh(&m.counts[e], cnt[e]);
     }
     lds_barrier();
     block_exscan(cnt, m.E, tmp);           // cnt -> tok_indptr
     const int nb = block_exscan(blk, m.E, tmp);
     for (int e = tid; e < m.E; e += kThreads) {
-      st_coh(&m.tok_indptr[e], cnt[e]);
-      st_coh(&m.blk_indptr[e], blk[e]);
-      st_coh(&m.task_indptr[e], blk[e] * nt1);
+      if (pub) {
+        st_coh(&m.tok_indptr[e], cnt[e]);
+        st_coh(&m.blk_indptr[e], blk[e]);
+        st_coh(&m.task_indptr[e], blk[e] * nt1);
+      }
       s_i[e] = s_i[1024 + e] = cnt[e] + bef[e];   // hs is no longer read
     }
-    if (tid == 0) {
+    if (pub && tid == 0) {
       st_coh(&m.tok_indptr[m.E], m.T * m.k);
       st_coh(&m.blk_indptr[m.E], nb);
       st_coh(&m.task_indptr[m.E], nb * nt1);
@@ -717,7 +733,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     auto gate = [&](int round) ET_INLINE -> bool {
       if (round != 0) return true;
       if ((sched == ET_SCHED_STATIC || sched == ET_SCHED_BARRIER) && !seen_group) {
-        if (!wg_wait(c, EV_GROUP, NR, task)) return false;
+        if (!wg_wait_bcast(c, EV_GROUP, EV_GROUP, task)) return false;
         seen_group = true;
       }
       for (int i = tid; i < rows; i += kThreads) {
@@ -781,7 +797,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     if (sched == ET_SCHED_PER_OP) return true;
     wg_release();
     if (sched == ET_SCHED_BARRIER) {
-      t0_notify(c, EV_G1ALL, 1, meta(MD_TOTAL1), task);
+      t0_notify_bcast(c, EV_G1ALL, EV_G1ALL, 1, meta(MD_TOTAL1), task);
     } else if (sched == ET_SCHED_STATIC) {
       t0_notify(c, m.ev_h + gb, 1, nt1, task);
     } else {
@@ -825,7 +841,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       if (sched == ET_SCHED_STATIC) {
         if (!wg_wait(c, m.ev_h + gb, nt1, task)) return false;
       } else if (sched == ET_SCHED_BARRIER && !seen_g1) {
-        if (!wg_wait(c, EV_G1ALL, meta(MD_TOTAL1), task)) return false;
+        if (!wg_wait_bcast(c, EV_G1ALL, EV_G1ALL, task)) return false;
         seen_g1 = true;
       }
       for (int i = tid; i < rows; i += kThreads) {
@@ -897,7 +913,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     wg_release();   // also completes wave 0's perm copy
     if (!cgrp && !inline_comb) {
       if (sched != ET_SCHED_DYNAMIC) {
-        t0_notify(c, EV_DOWN, 1, total2, task);
+        t0_notify_bcast(c, EV_DOWN, EV_DOWN, 1, total2, task);
       } else if (wg_notify(c, EV_DOWN, 1, total2, task)) {
         // the last down tile: push the combine tiles
         const int b3 = base1 + meta(MD_TOTAL1) + total2;
@@ -952,7 +968,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     if (comb_groups(total2)) {
       if (!wg_wait(c, m.ev_c + t3, comb_wait(tc, cc), task)) return false;
     } else if ((sched == ET_SCHED_STATIC || sched == ET_SCHED_BARRIER) && !seen_down) {
-      if (!wg_wait(c, EV_DOWN, meta(MD_TOTAL2), task)) return false;
+      if (!wg_wait_bcast(c, EV_DOWN, EV_DOWN, task)) return false;
       seen_down = true;
     }
     const int t0 = tc * kCombTok;
@@ -970,15 +986,20 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       if (sched == ET_SCHED_PER_OP) return true;
       if (sched == ET_SCHED_BARRIER) {
         wg_release();
-        t0_notify(c, EV_ROUTE, 1, NR, task);
+        t0_notify_bcast(c, EV_ROUTE, EV_ROUTE, 1, NR, task);
         return true;
       }
       // static / dynamic: once every chunk's histogram is out, this
       // workgroup scans and groups its own chunk
       if (!solo_route) {
         wg_release();
-        t0_notify(c, EV_ROUTE, 1, NR, task);
-        if (!wg_wait(c, EV_ROUTE, NR, task)) return false;
+        if (many_chunks) {
+          t0_notify_bcast(c, EV_ROUTE, EV_ROUTE, 1, NR, task);
+          if (!wg_wait_bcast(c, EV_ROUTE, EV_ROUTE, task)) return false;
+        } else {
+          t0_notify(c, EV_ROUTE, 1, NR, task);
+          if (!wg_wait(c, EV_ROUTE, NR, task)) return false;
+        }
       } else {
         t0_notify(c, EV_ROUTE, 1, NR, task);
       }
@@ -987,9 +1008,11 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       if (task == 0) {
         count_run(c, NR);
         trace_task(c, NR, ts);
-        if (sched == ET_SCHED_STATIC) {   // task totals are out: gemm tasks may start and prefetch weights
+        // static: task totals are out, gemm tasks may start and prefetch
+        // weights; dynamic: pushes of gemm tasks may go out
+        if (sched == ET_SCHED_STATIC || many_chunks) {
           wg_release();
-          t0_notify(c, EV_SCAN, 1, 1, NR);
+          t0_notify_bcast(c, EV_SCAN, EV_SCAN, 1, 1, NR);
         }
       }
       ts = trace_now(c);
@@ -998,14 +1021,14 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       trace_task(c, NR + 1 + task, ts);
       wg_release();
       if (sched == ET_SCHED_STATIC) {
-        t0_notify(c, EV_GROUP, 1, NR, task);
+        t0_notify_bcast(c, EV_GROUP, EV_GROUP, 1, NR, task);
         return true;
       }
       // dynamic: data-dependent notify targets -- the experts this chunk's
       // tokens chose, each decremented by this chunk's rows for it; the
       // experts whose events this completes have all their gate/up tiles
       // pushed in one piece (block-major within each expert)
-      set_total(c, NR + nb * (nt1 + nt2) + ncomb);
+      if (task == 0) set_total(c, NR + nb * (nt1 + nt2) + ncomb);
       const int* cur = s_i;
       const int* base = s_i + 1024;
       int* fe = s_i + 2048;     // fired experts
@@ -1026,6 +1049,9 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       __syncthreads();
       const int nf = sh.v[6];
       if (nf == 0) return true;
+      // the pushed tasks read the offsets chunk 0 publishes before EV_SCAN
+      // (few chunks: this chunk published them itself)
+      if (task != 0 && many_chunks && !wg_wait_bcast(c, EV_SCAN, EV_SCAN, task)) return false;
       auto nblk_of = [&](int e) ET_INLINE { return (e + 1 < m.E ? blk[e + 1] : nb) - blk[e]; };
       for (int i = tid; i < nf; i += kThreads) fpre[i] = nblk_of(fe[i]) * nt1;
       __syncthreads();
@@ -1050,20 +1076,20 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       return true;
     }
     if (task == NR) {   // the scan as a task of its own: barrier and per-op modes
-      if (sched == ET_SCHED_BARRIER && !wg_wait(c, EV_ROUTE, NR, task)) return false;
+      if (sched == ET_SCHED_BARRIER && !wg_wait_bcast(c, EV_ROUTE, EV_ROUTE, task)) return false;
       scan();
       if (sched == ET_SCHED_PER_OP) return true;
       wg_release();
-      t0_notify(c, EV_SCAN, 1, 1, task);
+      t0_notify_bcast(c, EV_SCAN, EV_SCAN, 1, 1, task);
       return true;
     }
     if (task < base1) {   // grouping tasks: barrier and per-op modes
       const int r = task - NR - 1;
-      if (sched == ET_SCHED_BARRIER && !wg_wait(c, EV_SCAN, 1, task)) return false;
+      if (sched == ET_SCHED_BARRIER && !wg_wait_bcast(c, EV_SCAN, EV_SCAN, task)) return false;
       group(r);
       if (sched == ET_SCHED_PER_OP) return true;
       wg_release();
-      t0_notify(c, EV_GROUP, 1, NR, task);
+      t0_notify_bcast(c, EV_GROUP, EV_GROUP, 1, NR, task);
       return true;
     }
     const int total1 = meta(MD_TOTAL1), total2 = meta(MD_TOTAL2);
@@ -1119,9 +1145,12 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       if (ok) count_run(c, NR + 1 + r);
       if (ok) trace_task(c, NR + 1 + r, t0);
     }
-    if (ok) ok = wg_wait(c, EV_SCAN, 1, -1);
+    if (ok) ok = wg_wait_bcast(c, EV_SCAN, EV_SCAN, -1);
     if (ok) {
+      // the task totals and the index tables of the first gemm task are
+      // requested in one memory round trip
       const int total1 = meta(MD_TOTAL1), total2 = meta(MD_TOTAL2);
+      load_cache();
       const int end = base1 + total1 + total2 + ncomb;
       for (int t = base1 + xcd_pos(c.wg, c.G); ok && t < end; t += c.G) {
         const long long t0 = trace_now(c);

@@ -35,8 +35,15 @@ enum : int {
   HDR_QTOTAL = 160,     // ready queue: total tasks of this call once known (else INT_MAX)
   HDR_EXIT = 192,       // workgroups that finished this call
   HDR_META = 224,       // 32 words of per-call workload metadata
-  HDR_WORDS = 256
+  HDR_FLAGS = 256,      // broadcast flags: [kBcastSlots][kBcastLines] lines of 32 words
+  HDR_WORDS = 256 + 8 * 64 * 32
 };
+// Broadcast events (a coarse event with many waiters): the notify that
+// completes one writes the call's generation into kBcastLines flag lines of
+// its slot, and each waiter polls the line of its own workgroup.
+constexpr int kBcastSlots = 8;
+constexpr int kBcastLines = 64;
+static_assert(HDR_WORDS == HDR_FLAGS + kBcastSlots * kBcastLines * 32, "flag region");
 constexpr size_t kHdrBytes = HDR_WORDS * 4;
 
 // Ready-queue shards (dynamic mode): control words of shard q at
@@ -142,6 +149,7 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kHistEntries = 8192;    // n_route * E must fit (int32, 32 KB of LDS)
 constexpr int kRouteTok = 8;          // tokens per routing chunk (fewer chunks when T is small)
+constexpr int kBcastChunks = 16;      // routing chunks from which their events are broadcast
 
 enum : int { EV_ROUTE = 0, EV_SCAN = 1, EV_GROUP = 2, EV_G1ALL = 3, EV_DOWN = 4, EV_FIXED = 8 };
 

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kThreads, 1) void splitk_kernel(RunArgs ra, SplitKA
       if (sched == ET_SCHED_PER_OP) return true;
       wg_release();
       if (sched == ET_SCHED_BARRIER) {
-        t0_notify(c, ev_all, 1, n1, task);
+        t0_notify_bcast(c, ev_all, 0, 1, n1, task);
       } else if (sched == ET_SCHED_STATIC) {
         t0_notify(c, i, 1, 4, task);
       } else if (wg_notify(c, i, 1, 4, task)) {
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kThreads, 1) void splitk_kernel(RunArgs ra, SplitKA
     if (sched == ET_SCHED_STATIC) {
       if (!wg_wait(c, i, 4, task)) return false;
     } else if (sched == ET_SCHED_BARRIER) {
-      if (!wg_wait(c, ev_all, n1, task)) return false;
+      if (!wg_wait_bcast(c, ev_all, 0, task)) return false;
     }
     splitk_stage2(s, i);
     return true;

@@ -139,6 +139,8 @@ def test_event_invariants(sched, T):
         assert (cnt[ev_exp:ev_exp + E] == -tab["events"]["E_exp"]["wait_count"]).all()
         assert (cnt[ev_he:ev_he + E] == -tab["events"]["E_he"]["wait_count"]).all()
         assert (cnt[ev_h:ev_h + nb] == 0).all()
+        # chunk 0 fires the scan event for the other chunks' pushes
+        assert cnt[1] == (-1 if nr >= 16 else 0) and cnt[2] == 0
     else:
         assert (cnt[ev_h:ev_h + nb] == -tab["events"]["E_h"]["wait_count"]).all()
         assert (cnt[ev_he:ev_he + E] == 0).all()
