@@ -215,6 +215,25 @@ def test_symbolic_token_counts_one_workspace():
             check_against_oracle("moe_skewed", T, out, aux)
 
 
+def test_schedules_interleaved_one_workspace():
+    """All four schedules in turn on one workspace, with the token count
+    changing: the coarse events' broadcast flags hold the generation of the
+    call that fired them, which grows with every call except the
+    per-operator baseline's (it runs no epilogue and waits on no event), so
+    a flag left by an earlier call must never pass for a fired event.  With
+    64 and 32 routing chunks (T=1024, 256) the routing event is a broadcast
+    event too; with 8 (T=64) it is polled on its counter."""
+    ws = _ws("moe_skewed", 1024)
+    seq = [("static", 1024), ("per_op", 256), ("static", 256), ("barrier", 1024),
+           ("per_op", 64), ("barrier", 64), ("dynamic", 1024), ("static", 1024),
+           ("per_op", 1024), ("dynamic", 256), ("static", 64)]
+    calls0 = ws.status()["calls"]
+    for sched, T in seq:
+        _, _, _, _, out, aux, _ = run_moe("moe_skewed", T, sched, ws=ws)
+        check_against_oracle("moe_skewed", T, out, aux)
+    assert ws.status()["calls"] == calls0 + sum(s != "per_op" for s, _ in seq)
+
+
 @pytest.mark.parametrize("sched", ["static", "dynamic"])
 def test_cooperative_launch(sched):
     """The cooperative launch mode runs the same kernel: same results."""
