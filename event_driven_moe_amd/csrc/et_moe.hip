@@ -1028,7 +1028,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       // tokens chose, each decremented by this chunk's rows for it; the
       // experts whose events this completes have all their gate/up tiles
       // pushed in one piece (block-major within each expert)
-      if (task == 0) set_total(c, NR + nb * (nt1 + nt2) + ncomb);
+      if (task == 0) set_total(c, nb * (nt1 + nt2) + ncomb);
       const int* cur = s_i;
       const int* base = s_i + 1024;
       int* fe = s_i + 2048;     // fired experts
@@ -1099,8 +1099,19 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   };
 
   if (sched == ET_SCHED_DYNAMIC) {
+    // routing chunk r runs on workgroup r, as under the static schedule:
+    // claiming the chunks from the queue put a contended atomic (every
+    // workgroup of a shard on one claim counter) before the front; the
+    // gemm and combine tasks come from the queue
+    bool ok = true;
+    for (int r = c.wg; ok && r < NR; r += c.G) {
+      const long long t0 = trace_now(c);
+      ok = run(r);
+      if (ok) count_run(c, r);
+      if (ok) trace_task(c, r, t0);
+    }
     PopState ps;
-    for (;;) {
+    while (ok) {
       const int t = wg_pop(c, ps);
       const long long t0 = trace_now(c);
       if (t < 0 || !run(t)) break;
@@ -1206,8 +1217,8 @@ int launch_moe(const LaunchCommon& lc, const float* logits, const uint16_t* x, i
   m.ev_h = mp.ev_h();
   m.ev_c = mp.ev_c();
   RunArgs ra = lc.run_args();
-  ra.n_init = m.NR;
-  ra.n_single = 2 * m.NR + 1;   // routing and grouping: one slot per claim
+  ra.n_init = 0;     // dynamic: routing runs on workgroups 0..NR-1; the queue holds pushed tasks only
+  ra.n_single = 0;
   ra.total_hint = kUnknownTotal;
   ra.extent = mp.extent(T, tl);
   const void* const kernels[] = {
