@@ -79,7 +79,8 @@ struct RunArgs {
   int fetch;           // dynamic: slots claimed per atomic
   int phase;           // per-op mode: operator this launch runs
   long long timeout;   // watchdog, 100 MHz ticks
-  int n_init;          // dynamic: tasks [0, n_init) are in the queue from the start
+  int init_base;       // dynamic: tasks [0, init_base) run on workgroups w, w + G, ... directly
+  int n_init;          // dynamic: tasks [init_base, init_base + n_init) are in the queue from the start
   int n_single;        // dynamic: slots below this index are claimed one at a time
   int total_hint;      // dynamic: total tasks when known at launch, else kUnknownTotal
   int extent;          // counters this call uses (a prefix of its bank)
@@ -387,7 +388,7 @@ __device__ __forceinline__ int shard_init(const RunArgs& a, int q) {
 __device__ __forceinline__ int resolve_slot(const Ctx& c, int q, int idx) {
   const RunArgs& a = c.a;
   const int n_init = shard_init(a, q);
-  if (idx < n_init) return q + a.nq * idx;
+  if (idx < n_init) return a.init_base + q + a.nq * idx;
   const int s = idx - n_init;
   int* p = &a.slots[(size_t)q * a.q_cap + s];
   long long t0 = 0;

@@ -132,8 +132,18 @@ __global__ __launch_bounds__(kThreads, kMlpOcc<MT>) void mlp_kernel(RunArgs ra, 
     // gate/up tile has already been claimed by a running worker: the down
     // tile may wait on its h events without risk of deadlock (the "early
     // push" of Event Tensor notes, section "动态调度").
+    // the first round of tasks runs on workgroup w = task id directly: a
+    // claim from the queue would put a contended atomic (every workgroup of
+    // a shard on one claim counter) before the first task
+    bool ok = true;
+    for (int t = c.wg; ok && t < ra.init_base; t += c.G) {
+      const long long t0 = trace_now(c);
+      ok = run(t);
+      if (ok) count_run(c, t);
+      if (ok) trace_task(c, t, t0);
+    }
     PopState ps;
-    for (;;) {
+    while (ok) {
       const int t = wg_pop(c, ps);
       const long long t0 = trace_now(c);
       if (t < 0 || !run(t)) break;
@@ -175,8 +185,9 @@ int launch_mlp(const LaunchCommon& lc, const uint16_t* x, int B, const uint16_t*
   m.ev_all = mp.n_events_max() - 1;
   const int n_gate = mb * (p->inter / 16), n_down = mb * (p->hidden / 16);
   RunArgs ra = lc.run_args();
-  ra.n_init = n_gate + n_down;
-  ra.total_hint = n_gate + n_down;
+  ra.init_base = n_gate + n_down < lc.G ? n_gate + n_down : lc.G;   // first round runs directly
+  ra.n_init = n_gate + n_down - ra.init_base;
+  ra.total_hint = n_gate + n_down - ra.init_base;
   ra.extent = mp.n_events_max();
   const void* k = tv == TV_M16   ? reinterpret_cast<const void*>(&mlp_kernel<1>)
                   : tv == TV_M32 ? reinterpret_cast<const void*>(&mlp_kernel<2>)

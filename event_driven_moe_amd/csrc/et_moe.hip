@@ -1104,7 +1104,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     // workgroup of a shard on one claim counter) before the front; the
     // gemm and combine tasks come from the queue
     bool ok = true;
-    for (int r = c.wg; ok && r < NR; r += c.G) {
+    for (int r = c.wg; ok && r < ra.init_base; r += c.G) {
       const long long t0 = trace_now(c);
       ok = run(r);
       if (ok) count_run(c, r);
@@ -1217,7 +1217,8 @@ int launch_moe(const LaunchCommon& lc, const float* logits, const uint16_t* x, i
   m.ev_h = mp.ev_h();
   m.ev_c = mp.ev_c();
   RunArgs ra = lc.run_args();
-  ra.n_init = 0;     // dynamic: routing runs on workgroups 0..NR-1; the queue holds pushed tasks only
+  ra.init_base = m.NR;   // dynamic: routing runs on workgroups 0..NR-1
+  ra.n_init = 0;         // the queue holds pushed tasks only
   ra.n_single = 0;
   ra.total_hint = kUnknownTotal;
   ra.extent = mp.extent(T, tl);

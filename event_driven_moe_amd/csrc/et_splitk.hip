@@ -78,8 +78,18 @@ __global__ __launch_bounds__(kThreads, 1) void splitk_kernel(RunArgs ra, SplitKA
 
   const int total = 5 * s.n;
   if (sched == ET_SCHED_DYNAMIC) {
+    // the first round of tasks runs on workgroup w = task id directly: a
+    // claim from the queue would put a contended atomic (every workgroup of
+    // a shard on one claim counter) before the first task
+    bool ok = true;
+    for (int t = c.wg; ok && t < ra.init_base; t += c.G) {
+      const long long t0 = trace_now(c);
+      ok = run(t);
+      if (ok) count_run(c, t);
+      if (ok) trace_task(c, t, t0);
+    }
     PopState ps;
-    for (;;) {
+    while (ok) {
       const int t = wg_pop(c, ps);
       const long long t0 = trace_now(c);
       if (t < 0 || !run(t)) break;
@@ -115,8 +125,9 @@ __global__ __launch_bounds__(kThreads, 1) void splitk_kernel(RunArgs ra, SplitKA
 int launch_splitk(const LaunchCommon& lc, const float* A, int rows, float* B, float* C) {
   SplitKArgs s{A, B, C, rows / 32, lc.plan->max_tokens / 32};
   RunArgs ra = lc.run_args();
-  ra.n_init = 4 * s.n;
-  ra.total_hint = 5 * s.n;
+  ra.init_base = 4 * s.n < lc.G ? 4 * s.n : lc.G;   // stage-1 tiles run directly, then from the queue
+  ra.n_init = 4 * s.n - ra.init_base;
+  ra.total_hint = 5 * s.n - ra.init_base;          // queue tasks: the rest of stage 1 and stage 2
   ra.extent = s.n_max + 1;
   if (lc.sched == ET_SCHED_PER_OP) {
     for (int ph = 0; ph < 2; ++ph) {
