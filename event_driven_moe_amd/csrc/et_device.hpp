@@ -209,6 +209,26 @@ __device__ __forceinline__ bool wg_probe_range(const Ctx& c, int first, int n, i
   return wg_bcast(c, all, 1) != 0;
 }
 
+// Non-blocking: how many of events [first, first + n), counted from the
+// first, have fired?  One memory round trip per 64 events (wave 0's lanes),
+// result broadcast.
+__device__ __forceinline__ int wg_probe_prefix(const Ctx& c, int first, int n, int wait_count) {
+  int done = n;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    for (int base = 0; base < n; base += 64) {
+      const bool mine = base + lane < n;
+      const int v = mine ? ld_rlx(c.ev + first + base + lane) : -wait_count;
+      const unsigned long long pending = __ballot(v != -wait_count);
+      if (pending != 0) {
+        done = base + __builtin_ctzll(pending);
+        break;
+      }
+    }
+  }
+  return wg_bcast(c, done, 1);
+}
+
 // Complete this workgroup's stores (every wave), then synchronise the
 // workgroup.  Precedes every notify and push.
 __device__ __forceinline__ void wg_release() {

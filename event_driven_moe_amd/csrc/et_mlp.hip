@@ -99,19 +99,23 @@ __global__ __launch_bounds__(kThreads, kMlpOcc<MT>) void mlp_kernel(RunArgs ra, 
     const Rsrc rb[1] = {make_rsrc(m.wd, (uint32_t)m.H * m.I * 2)};
     const uint32_t bo[1] = {(uint32_t)(16 * n2 + (lane & 15)) * (uint32_t)(m.I * 2)};
     const int nkb = m.I / kKBlock;
-    bool ready = sched == ET_SCHED_PER_OP;
+    // K-blocks (h tiles) known complete.  A poll inside the weight stream
+    // completes only after every load its wave issued before it (loads
+    // complete in order), so a round inside the known-complete prefix polls
+    // nothing; the first round beyond it counts the complete h tiles from
+    // there on (one round trip for all of them) and waits only if its own
+    // are not among them.
+    int ready_kb = sched == ET_SCHED_PER_OP ? nkb : 0;
     auto gate = [&](int round) ET_INLINE -> bool {
-      if (ready) return true;
       if (sched == ET_SCHED_BARRIER) return round > 0 || wg_wait_bcast(c, m.ev_all, 0, task);
-      // one round trip checks every h tile of the row block; if some are not
-      // done yet, wait only for the K-blocks of the coming round
-      if (round == 0 && wg_probe_range(c, b * nht, nht, kHTile / 16)) {
-        ready = true;
-        return true;
-      }
       const int k0 = round * 4;
       const int nk = nkb - k0 < 4 ? nkb - k0 : 4;
-      return wg_wait_range(c, b * nht + k0, nk, kHTile / 16, task);
+      if (k0 + nk <= ready_kb) return true;
+      ready_kb = k0 + wg_probe_prefix(c, b * nht + k0, nht - k0, kHTile / 16);
+      if (k0 + nk <= ready_kb) return true;
+      if (!wg_wait_range(c, b * nht + k0, nk, kHTile / 16, task)) return false;
+      ready_kb = k0 + nk;
+      return true;
     };
     Tile2 tile;
     if (!tile.run(ra_, rows_off, rb, bo, nkb, gate, red)) return false;
