@@ -1,14 +1,15 @@
 """Benchmark of the Event Tensor MoE megakernel on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--tokens T]
-                [--sched dynamic|static|barrier|per_op] [--modes] [--no-cpu]
+                [--sched static|dynamic|barrier|per_op] [--no-modes] [--no-cpu]
 
 Prints ONE JSON line.  A step is one whole MoE layer (routing -> grouping ->
 grouped gate/up GEMM -> grouped down GEMM -> combine) on one batch of seeded
-synthetic input already resident in HBM.  The default workload is the
-Qwen3-30B-A3B-shaped layer of the Event Tensor MoE experiment (hidden 2048,
-128 experts, top-8, expert intermediate 768) at 1024 tokens with Zipf-skewed
-routing, under the dynamic schedule with 4 slots claimed per atomic.
+synthetic input already resident in HBM.  The default workload is the large
+MoE layer (hidden 7168, 256 experts, top-8, expert intermediate 2048, 22.5 GB
+of bf16 expert weights resident in HBM, per-batch random router bias) at
+8192 tokens, the largest layer that fits one GPU; `value` is its throughput
+under --sched, and every schedule's time per layer is reported in `config`.
 """
 
 import argparse
@@ -66,7 +67,9 @@ def time_calls(fn, steps, warmup):
 
 def cpu_baseline(cfg, logits, x, wg, wu, wd, T, target_s=15.0):
     """The oracle (fp64, numpy) on a bounded sample of the same workload's
-    tokens; tokens/s scaled from the sample."""
+    tokens: tokens/s of the sample.  Only the experts the sampled tokens are
+    routed to are copied to the host, one at a time as the oracle asks for
+    them (the large layer's full weight set would be 45 GB in fp32)."""
     import numpy as np
     from oracle import moe as omoe
     try:
@@ -76,34 +79,33 @@ def cpu_baseline(cfg, logits, x, wg, wu, wd, T, target_s=15.0):
         threads = os.cpu_count()
     L = logits.cpu().numpy()
     X = x.float().cpu().numpy()
-    cache = {}
+    k = cfg["top_k"]
 
     def weights(e):
-        if e not in cache:
-            cache[e] = (wg[e].t().float().cpu().numpy(), wu[e].t().float().cpu().numpy(),
-                        wd[e].t().float().cpu().numpy())
-        return cache[e]
-    # host copies of every expert's weights first (not oracle work)
-    for e in range(cfg["n_experts"]):
-        weights(e)
-    rng = np.random.default_rng(0)
-    n = min(T, 16)
+        return (wg[e].t().float().cpu().numpy(), wu[e].t().float().cpu().numpy(),
+                wd[e].t().float().cpu().numpy())
+
+    ids, _ = omoe.route(L, k)
+    order = np.random.default_rng(0).permutation(T)
+    experts_of = lambda n: len(np.unique(ids[order[:n]]))
+    # a first pass over two tokens prices one expert; the sample is then the
+    # largest prefix of the shuffled tokens whose experts fit target_s
+    n = min(T, 2)
     t0 = time.perf_counter()
-    omoe.moe_layer(L, X, cfg["top_k"], weights, tokens=rng.choice(T, n, replace=False))
-    dt = time.perf_counter() - t0
-    # a token sample sized for about target_s of oracle work, repeated
-    # until that much time has passed
-    n2 = int(min(T, max(n, n * target_s / max(dt, 1e-3))))
-    sample = np.sort(rng.choice(T, n2, replace=False))
+    omoe.moe_layer(L, X, k, weights, tokens=np.sort(order[:n]))
+    per_expert = (time.perf_counter() - t0) / experts_of(n)
+    while n < T and experts_of(min(T, 2 * n)) * per_expert <= target_s:
+        n = min(T, 2 * n)
+    sample = np.sort(order[:n])
     reps = 0
     t0 = time.perf_counter()
-    while reps == 0 or time.perf_counter() - t0 < target_s:
-        omoe.moe_layer(L, X, cfg["top_k"], weights, tokens=sample)
+    while reps == 0 or time.perf_counter() - t0 < target_s / 2:
+        omoe.moe_layer(L, X, k, weights, tokens=sample)
         reps += 1
     dt = time.perf_counter() - t0
-    return {"value": reps * n2 / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": "%d pass(es) over %d of %d tokens (each pass routes and groups all %d), "
-                      "fp64 numpy, %.1f s" % (reps, n2, T, T, dt)}
+    return {"value": reps * n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d pass(es) over %d of %d tokens (%d experts; each pass routes and groups "
+                      "all %d tokens), fp64 numpy, %.1f s" % (reps, n, T, experts_of(n), T, dt)}
 
 
 COPY_BYTES = 1 << 30   # calibration copy: reads and writes 1 GiB
@@ -189,13 +191,14 @@ def traffic_summary(fetch_db, write_db, key):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="moe_skewed")
-    ap.add_argument("--tokens", type=int, default=1024)
-    ap.add_argument("--sched", default="dynamic")
+    ap.add_argument("--workload", default="moe_large")
+    ap.add_argument("--tokens", type=int, default=8192)
+    ap.add_argument("--sched", default="static")
     ap.add_argument("--fetch", type=int, default=4)
-    ap.add_argument("--modes", action="store_true", help="also time the other schedules")
+    ap.add_argument("--no-modes", action="store_true",
+                    help="time only --sched (default: every schedule, reported in config)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy before timing (reference for HBM counters)")
@@ -223,6 +226,8 @@ def main():
     dev = "cuda"
     cfg = synth.MOE_PRESETS[args.workload]
     T = args.tokens
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    log("bench: %s T=%d, generating inputs" % (args.workload, T))
     logits, x = synth.moe_activations(cfg, T, device=dev)
     wg, wu, wd = synth.moe_weights_k_major(cfg, device=dev)
     ws = et.Workspace(et.WL_MOE, T, cfg["hidden"], cfg["inter"], cfg["n_experts"],
@@ -245,6 +250,7 @@ def main():
     if args.copy_calibration:
         copy_calibration()
     torch.cuda.synchronize()
+    log("bench: timing %d steps of %s" % (args.steps, args.sched))
     per, wall = time_calls(step, args.steps, args.warmup)
     torch.cuda.synchronize()
     if ws.status()["status"] != 0:
@@ -277,11 +283,16 @@ def main():
                 "traffic": traffic}
 
     modes = {}
-    if args.modes:
+    if not args.no_modes:
         for s in ("static", "dynamic", "barrier", "per_op"):
+            log("bench: timing schedule %s" % s)
             p, _ = time_calls(lambda: step(s), max(10, args.steps // 2), 3)
             modes[s] = round(1e3 * sum(p) / len(p), 2)
+        if ws.status()["status"] != 0:
+            raise SystemExit("device fault while timing the schedules")
 
+    bias = {"zipf": ", Zipf-skewed router bias (scale %g)" % cfg.get("zipf_scale", 0),
+            "random": ", per-batch N(0,1) router bias", "none": ""}[cfg["bias"]]
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -290,14 +301,18 @@ def main():
         "config": {
             "workload": "%s: MoE layer, %d tokens, hidden %d, %d experts, top-%d, "
                         "intermediate %d%s" % (args.workload, T, cfg["hidden"], cfg["n_experts"],
-                                               cfg["top_k"], cfg["inter"],
-                                               ", Zipf-skewed router bias" if cfg["bias"] == "zipf" else ""),
-            "tokens": T, "schedule": args.sched, "fetch_batch": args.fetch,
+                                               cfg["top_k"], cfg["inter"], bias),
+            "tokens": T, "schedule": args.sched,
+            "fetch_batch_cap": args.fetch,
+            "fetch_batch_note": "dynamic schedule: at most this many queue slots per claim; a "
+                                "claim takes no more than the worker's share of the published slots",
             "active_experts": n_active, "max_rows_per_expert": max_rows,
+            "us_per_layer_mean": round(1e3 * ms, 2),
             "us_per_layer_median": round(1e3 * per_sorted[len(per) // 2], 2),
             "us_per_layer_p10": round(1e3 * per_sorted[len(per) // 10], 2),
             "us_per_layer_p90": round(1e3 * per_sorted[(9 * len(per)) // 10], 2),
             "algorithmic_bytes": alg["bytes"], "flops": alg["flops"],
+            "arithmetic_intensity": round(ai, 1),
             "mfma_frac": round(achieved_tfs / MFMA_BF16_PEAK_TFS, 4),
             "hbm_frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
             "kernel": "moe_kernel (one persistent launch per layer)",
@@ -306,7 +321,11 @@ def main():
     }
     if modes:
         res["config"]["us_per_layer_by_schedule"] = modes
+        res["config"]["schedules"] = ("static: per-CU task lists; dynamic: on-device ready queue; "
+                                      "barrier: same tasks, one event per operator; per_op: one "
+                                      "kernel launch per operator")
     if not args.no_cpu:
+        log("bench: oracle CPU baseline")
         res["cpu_baseline"] = cpu_baseline(cfg, logits, x, wg, wu, wd, T)
     print(json.dumps(res))
 

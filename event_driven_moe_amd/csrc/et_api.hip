@@ -35,15 +35,13 @@ RunArgs LaunchCommon::run_args() const {
 
 // Clears [0, bytes) of the workspace and writes the header (no memset node,
 // so the call can also sit in a captured graph).
+// Every word is written exactly once, by the one thread whose grid-stride
+// loop reaches it, so no two stores to a word race.
 __global__ void ws_init_kernel(int* ws, size_t words, int workload) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < words;
        i += (size_t)gridDim.x * blockDim.x)
-    ws[i] = 0;
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    ws[HDR_MAGIC] = kMagic;
-    ws[HDR_WORKLOAD] = workload;
-    ws[HDR_QTOTAL] = kUnknownTotal;
-  }
+    ws[i] = i == HDR_MAGIC ? kMagic : i == HDR_WORKLOAD ? workload
+          : i == HDR_QTOTAL ? kUnknownTotal : 0;
 }
 
 namespace {

@@ -59,17 +59,22 @@ inline int pick_mlp_tile(int batch, int forced) {
 // an expert at most once); few rows -> narrow stream tiles (their tasks are
 // short, so the weights of a small expert spread over many CUs), many routed
 // rows in total -> wide LDS-staged MFMA tiles (each weight byte feeds more
-// rows).  `forced` (0 .. TV_COUNT-1) overrides.
-inline int pick_moe_tile(int tokens, int top_k, int n_experts, int forced) {
+// rows).  `forced` (0 .. TV_COUNT-1) overrides.  The wide variants' down
+// tasks cover 256 output columns, so they serve only hidden sizes that are a
+// multiple of 256 (the rule falls back to the 64-row stream variant).
+inline bool moe_tile_fits(int tv, int hidden, int inter) {
+  const Tiling t = tiling_of(tv);
+  return hidden % t.bn2 == 0 && inter % t.bn1 == 0;
+}
+inline int pick_moe_tile(int tokens, int top_k, int hidden, int inter, int forced) {
   if (forced >= 0 && forced < TV_COUNT) return forced;
-  (void)n_experts;
   // 64-column down tasks once 16 or more (token, expert) pairs are routed
   // (typically 8+ row blocks, so 256+ such tasks); with fewer rows the
   // 16-column ones keep every CU busy
   if (tokens <= 32) return tokens * top_k >= 16 ? TV_M16W : TV_M16;
-  if (tokens * top_k <= 256) return TV_M64;
-  if (tokens <= 512) return TV_W64;
-  return TV_W128;
+  const int wide = tokens <= 512 ? TV_W64 : TV_W128;
+  if (tokens * top_k <= 256 || !moe_tile_fits(wide, hidden, inter)) return TV_M64;
+  return wide;
 }
 
 }  // namespace et

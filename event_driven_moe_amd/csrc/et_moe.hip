@@ -57,7 +57,6 @@ struct MoeArgs {
   int* tok_indptr;
   int* blk_indptr;
   int* task_indptr;
-  int* blk_expert;
   int* perm;
   int* inv;
   uint16_t* h;
@@ -1181,7 +1180,8 @@ int launch_moe(const LaunchCommon& lc, const float* logits, const uint16_t* x, i
              moe_n_route(p->n_experts)};
   const MoeAux ax = moe_aux_layout(mp);
   char* aux = lc.ws + p->off_aux;
-  const int tv = pick_moe_tile(T, p->top_k, p->n_experts, lc.tile);
+  const int tv = pick_moe_tile(T, p->top_k, p->hidden, p->inter, lc.tile);
+  if (!moe_tile_fits(tv, p->hidden, p->inter)) return ET_EUNSUPPORTED;
   const Tiling tl = tiling_of(tv);
   MoeArgs m;
   m.logits = logits;
@@ -1197,7 +1197,6 @@ int launch_moe(const LaunchCommon& lc, const float* logits, const uint16_t* x, i
   m.tok_indptr = reinterpret_cast<int*>(aux + ax.tok_indptr);
   m.blk_indptr = reinterpret_cast<int*>(aux + ax.blk_indptr);
   m.task_indptr = reinterpret_cast<int*>(aux + ax.task_indptr);
-  m.blk_expert = reinterpret_cast<int*>(aux + ax.blk_expert);
   m.perm = reinterpret_cast<int*>(aux + ax.perm);
   m.inv = reinterpret_cast<int*>(aux + ax.inv);
   m.h = reinterpret_cast<uint16_t*>(aux + ax.h);

@@ -31,7 +31,6 @@ enum : int {
   HDR_ERR_B = 66,
   HDR_ERR_C = 67,
   HDR_QHEAD = 96,       // ready queue: implicit initial tasks claimed
-  HDR_QPUSH = 128,      // (unused)
   HDR_QTOTAL = 160,     // ready queue: total tasks of this call once known (else INT_MAX)
   HDR_EXIT = 192,       // workgroups that finished this call
   HDR_META = 224,       // 32 words of per-call workload metadata
@@ -154,7 +153,7 @@ constexpr int kBcastChunks = 16;      // routing chunks from which their events 
 enum : int { EV_ROUTE = 0, EV_SCAN = 1, EV_GROUP = 2, EV_G1ALL = 3, EV_DOWN = 4, EV_FIXED = 8 };
 
 // per-call metadata words (HDR_META + i), written by the scan task
-enum : int { MD_NB = 0, MD_TOTAL1 = 1, MD_TOTAL2 = 2, MD_NCOMB = 3 };
+enum : int { MD_NB = 0, MD_TOTAL1 = 1, MD_TOTAL2 = 2 };
 
 struct MoePlan {
   int t_max, hidden, inter, n_experts, top_k, n_route;
@@ -187,8 +186,8 @@ ET_HD int moe_n_route(int n_experts) {
 
 // Byte offsets of the MoE intermediates inside the aux region.
 struct MoeAux {
-  size_t topk_ids, topk_w, hist, counts, tok_indptr, blk_indptr, task_indptr, blk_expert,
-      perm, inv, h, y, bytes;
+  size_t topk_ids, topk_w, hist, counts, tok_indptr, blk_indptr, task_indptr, perm, inv, h, y,
+      bytes;
 };
 
 inline MoeAux moe_aux_layout(const MoePlan& p) {
@@ -203,7 +202,6 @@ inline MoeAux moe_aux_layout(const MoePlan& p) {
   a.tok_indptr = take((size_t)(p.n_experts + 1) * 4);
   a.blk_indptr = take((size_t)(p.n_experts + 1) * 4);
   a.task_indptr = take((size_t)(p.n_experts + 1) * 4);
-  a.blk_expert = take((size_t)p.nb_max() * 4);
   a.perm = take(TK * 4);
   a.inv = take(TK * 4);
   a.h = take(TK * p.inter * 2);

@@ -247,7 +247,7 @@ def moe_layer(logits, x, w_gate, w_up, w_down, out, ws, sched="dynamic", stream=
 
 def moe_aux(ws, T, intermediates=False):
     """Routing results and grouping of the last call (views into the workspace);
-    with ``intermediates``, also h (bf16 [T*k, I]) and y (float [T*k, H]), the
+    with ``intermediates``, also h (bf16 [T*k, I]) and y (bf16 [T*k, H]), the
     grouped rows of the two projections."""
     lay = ws.layout(T)
     k, E = ws.plan.top_k, ws.plan.n_experts

@@ -36,10 +36,15 @@ MOE_SMALL = dict(name="moe_small", hidden=2048, inter=1408, n_experts=8, top_k=2
 MOE_SKEWED = dict(name="moe_skewed", hidden=2048, inter=768, n_experts=128, top_k=8,
                   tokens=(64, 256, 1024), seed_logits=401, seed_x=402, seed_w=403,
                   bias="zipf", zipf_scale=1.5, zipf_exp=1.2)
+# The skewed layer's bias formula taken literally (scale 1.5) gives the
+# hottest expert every token (max/mean load E/k = 16); the same formula with
+# scale 0.15 gives the 3-4x max/mean load its description states.  Both are
+# kept: same shapes, seeds and weights, only the bias scale differs.
+MOE_SKEWED_CAL = dict(MOE_SKEWED, name="moe_skewed_cal", zipf_scale=0.15)
 MOE_LARGE = dict(name="moe_large", hidden=7168, inter=2048, n_experts=256, top_k=8,
                  tokens=(512, 2048, 8192), seed_logits=501, seed_x=502, seed_w=503,
                  seed_bias=504, bias="random")
-MOE_PRESETS = {c["name"]: c for c in (MOE_SMALL, MOE_SKEWED, MOE_LARGE)}
+MOE_PRESETS = {c["name"]: c for c in (MOE_SMALL, MOE_SKEWED, MOE_SKEWED_CAL, MOE_LARGE)}
 
 WEIGHT_STD = 0.02
 

@@ -99,9 +99,8 @@ typedef struct et_opts {
   int tile;          /* MoE / MLP tile-variant override (-1 = chosen from the token count) */
   int launch;        /* ET_LAUNCH_* (default ET_LAUNCH_ORDINARY) */
   int queue_shards;  /* dynamic mode: ready-queue shards, 1 (one central queue) or 8 (one per
-                        XCD: a pushed task goes to the shard its weight tile hashes to, workers
-                        pop their own XCD's shard first and take from the others when it is
-                        empty); 0 = default (8) */
+                        XCD: a pushed task goes to the shard its weight tile hashes to, and a
+                        worker pops only the shard of its own XCD); 0 = default (8) */
 } et_opts;
 
 /* Workspace plan: dimensions and byte offsets of every region.  Filled by
@@ -207,7 +206,11 @@ int et_mlp(const uint16_t* x, int n_tokens, const uint16_t* w_gate, const uint16
  * the permutation stay in the workspace (et_workspace_layout).  Grouping tasks notify
  * the events of the experts their tokens selected (data-dependent targets); in dynamic
  * mode the notify that zeroes expert e's event pushes its task range
- * tasks[task_indptr[e] : task_indptr[e+1]].  Deterministic: no float atomics. */
+ * tasks[task_indptr[e] : task_indptr[e+1]].  Deterministic: no float atomics.
+ * H and I must be multiples of 128 (checked when the workspace is planned).  The
+ * tile variant follows the token count unless et_opts.tile forces one; a forced
+ * variant whose column tiles do not divide H or I (the wide variants 3 and 4 cover
+ * 256 output columns per down task) returns ET_EUNSUPPORTED and enqueues nothing. */
 int et_moe_layer(const float* logits, const uint16_t* x, int n_tokens,
                  const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                  float* out, void* ws, const et_plan* plan, int sched,

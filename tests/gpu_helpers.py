@@ -35,11 +35,16 @@ def to_np(t):
     return t.detach().float().cpu().numpy() if t.dtype == torch.bfloat16 else t.detach().cpu().numpy()
 
 
+def moe_weights(name):
+    """Device weights of a preset, cached per weight set (presets that differ
+    only in their router bias share one copy)."""
+    cfg = synth.MOE_PRESETS[name]
+    return _moe_weights(cfg["hidden"], cfg["inter"], cfg["n_experts"], cfg["seed_w"])
+
+
 @functools.lru_cache(maxsize=2)
-def moe_weights(name, hidden=None, inter=None, n_experts=None):
-    cfg = dict(synth.MOE_PRESETS[name])
-    if hidden:
-        cfg.update(hidden=hidden, inter=inter, n_experts=n_experts)
+def _moe_weights(hidden, inter, n_experts, seed_w):
+    cfg = dict(hidden=hidden, inter=inter, n_experts=n_experts, seed_w=seed_w)
     return synth.moe_weights_k_major(cfg, device=DEV)
 
 

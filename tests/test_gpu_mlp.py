@@ -5,7 +5,7 @@ import pytest
 import torch
 
 from event_driven_moe_amd import et, synth
-from oracle import mlp as om
+from oracle import mlp as om, events as oev
 from gpu_helpers import DEV, SCHEDS, say, assert_rel, to_np
 
 pytestmark = pytest.mark.gpu
@@ -93,20 +93,25 @@ def test_modes_bit_identical(ws, weights):
 
 
 def test_invariants(ws, weights):
+    """Each task ran exactly once and every E_h counter ended at its wait
+    count, both as the oracle's event table states for the library's tiling
+    (rows per block 16/32/64 for B <= 16/32/64, 16-column gate/up and down
+    tiles, one event per 128-column h tile, the down tile covering all of K)."""
     wg, wu, wd, wgT, wuT, wdT = weights
-    for B, sched in ((64, "static"), (5, "dynamic"), (16, "static")):
+    for B, sched in ((64, "static"), (5, "dynamic"), (16, "static"), (33, "dynamic")):
         ws.runs().zero_()
         x = synth.normal_bf16((B, H), 1.0, B, DEV)
         _run(ws, x, wgT, wuT, wdT, sched, debug=et.DEBUG_COUNTS)
         st = ws.status()
-        mt = 1 if B <= 16 else (2 if B <= 32 else 4)
-        mb = -(-B // (16 * mt))
-        ntask = mb * (I // 16 + H // 16)
+        rows = 16 if B <= 16 else (32 if B <= 32 else 64)
+        tab = oev.mlp_table(B, H, I, rows, 16, 128, 16, 1)
+        ntask = sum(tab["tasks"].values())
+        assert st["last_tasks"] == ntask
         runs = ws.runs().cpu().numpy()
         assert (runs[:ntask] == 1).all() and (runs[ntask:] == 0).all()
         cnt = ws.counters(1 - st["bank"]).cpu().numpy()
-        nht = I // 128
-        assert (cnt[:mb * nht] == -8).all() and (cnt[mb * nht:-1] == 0).all()
+        wc = tab["events"]["E_h"]["wait_count"].reshape(-1)
+        assert (cnt[:wc.size] == -wc).all() and (cnt[wc.size:-1] == 0).all()
 
 
 @pytest.mark.parametrize("sched", ["static", "dynamic"])

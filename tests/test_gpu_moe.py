@@ -43,20 +43,32 @@ def _oracle(name, T):
     return omoe.moe_layer(to_np(logits), to_np(x), cfg["top_k"], moe_oracle_weights(wg, wu, wd))
 
 
-def check_against_oracle(name, T, out, aux):
-    ref = _oracle(name, T)
+def check_routing(aux, ref, k, inter, T, tile=-1):
+    """Integer outputs bit-exact (ids, counts, CSR offsets of rows and of the
+    gate/up tasks of the tiling the call used, the permutation and its
+    inverse); routing weights within 1e-5 of the largest."""
     assert np.array_equal(aux["ids"], ref["ids"]), "topk ids"
     assert np.array_equal(aux["counts"], ref["counts"]), "counts"
     assert np.array_equal(aux["tok_indptr"], ref["tok_indptr"]), "tok_indptr"
     assert np.array_equal(aux["perm"], ref["perm"]), "perm"
     assert np.array_equal(aux["inv"], ref["inv"]), "inv"
+    rows, bn1, _ = moe_tiling(T, k, tile)
+    assert np.array_equal(aux["task_indptr"], omoe.task_indptr(ref["counts"], rows, inter // bn1)), \
+        "task_indptr"
     assert np.abs(aux["w"] - ref["w"]).max() <= 1e-5 * np.abs(ref["w"]).max(), "topk_w"
+
+
+def check_against_oracle(name, T, out, aux, tile=-1):
+    cfg = synth.MOE_PRESETS[name]
+    ref = _oracle(name, T)
+    check_routing(aux, ref, cfg["top_k"], cfg["inter"], T, tile)
     assert_rel(out, ref["out"], 1e-2, "out")
     return ref
 
 
 CASES = [("moe_small", 1), ("moe_small", 8), ("moe_small", 32),
-         ("moe_skewed", 64), ("moe_skewed", 256), ("moe_skewed", 1024)]
+         ("moe_skewed", 64), ("moe_skewed", 256), ("moe_skewed", 1024),
+         ("moe_skewed_cal", 64), ("moe_skewed_cal", 256), ("moe_skewed_cal", 1024)]
 
 
 @pytest.mark.parametrize("sched", SCHEDS)
@@ -73,12 +85,12 @@ def test_modes_bit_identical(name, T):
         assert np.array_equal(o, outs[0])
 
 
-def moe_tiling(T, k, tile=-1):
+def moe_tiling(T, k, tile=-1, hidden=2048):
     """(rows per block, h columns per gate/up task, columns per down task) of
     the library's tile variant for T tokens routed to k experts each (or the
-    forced variant)."""
-    tv = tile if tile >= 0 else ((5 if T * k >= 16 else 0) if T <= 32 else 2 if T * k <= 256 else
-                                 3 if T <= 512 else 4)
+    forced variant); the wide variants need a hidden size divisible by 256."""
+    tv = tile if tile >= 0 else ((5 if T * k >= 16 else 0) if T <= 32 else
+                                 2 if T * k <= 256 or hidden % 256 else 3 if T <= 512 else 4)
     return {0: (16, 16, 16), 1: (32, 16, 16), 2: (64, 16, 16), 3: (64, 128, 256),
             4: (128, 128, 256), 5: (16, 16, 64)}[tv]
 
@@ -88,7 +100,7 @@ def moe_tiling(T, k, tile=-1):
 @pytest.mark.parametrize("T", [64, 1024])
 def test_tile_variants(tile, sched, T):
     _, _, _, _, out, aux, _ = run_moe("moe_skewed", T, sched, tile=tile)
-    check_against_oracle("moe_skewed", T, out, aux)
+    check_against_oracle("moe_skewed", T, out, aux, tile=tile)
 
 
 @pytest.mark.parametrize("fetch", [1, 8])
@@ -148,46 +160,79 @@ def test_event_invariants(sched, T):
     check_against_oracle(name, T, out, aux)
 
 
-def _exact_case(k, E=4, H=256, I=256, T=50, seed=0):
-    """Integer experts: x in {0,1} with x[:,0]=1; gate row 0 in [16,40) so
-    SiLU(g) == g below bf16 precision; |u| <= 3, so h = g*u exactly (|h| <=
-    117); two +-1 entries per down column, so every y is an integer with
-    |y| <= 234, exact in bf16 (the layer keeps y, the down projection's rows,
-    in bf16 like h).  Logits make the kept weights exactly 1 (k = 1) or 1/2
-    (two tied maxima, k = 2)."""
+def _exact_case(k, mode, E=4, H=512, I=256, T=50, seed=0):
+    """Integer experts whose every intermediate is exact: x in {0,1} with
+    x[:,0] = 1, so the gate row 0 of W_gate sets g exactly; g >= 16 makes
+    SiLU(g) equal g far below bf16 precision, so h = g*u and y = h Wd are
+    exact whenever they are representable in bf16 (the layer rounds h and
+    the down projection's rows y to bf16).
+
+    mode "mixed": g in [16, 40), three +-1 entries per up column (|u| <= 3),
+    two +-1 entries per down column (|y| <= 234).
+    mode "up_dense": g = 16, the up projection dense in {-1, 0, 1} (every
+    K-block of the gate/up tile contributes; h = 16 u), one +-1 entry per
+    down column (y_j = +-h_i).
+    mode "down_dense": g = 16, one +-1 entry per up column (h in {0, +-16}),
+    the down projection dense in {-1, 0, 1} over I = 256 (y = 16 n with
+    |n| <= 256, so every K-block of the down tile contributes exactly).
+
+    Logits make the kept weights exactly 1 (k = 1) or 1/2 (two tied maxima,
+    k = 2), so the combine is exact too."""
     g = torch.Generator(device="cpu").manual_seed(seed)
     x = torch.randint(0, 2, (T, H), generator=g).float()
     x[:, 0] = 1
     wg = torch.zeros(E, H, I)
-    wg[:, 0, :] = torch.randint(16, 40, (E, I), generator=g).float()
+    if mode == "mixed":
+        wg[:, 0, :] = torch.randint(16, 40, (E, I), generator=g).float()
+    else:
+        wg[:, 0, :] = 16.0
     wu = torch.zeros(E, H, I)
-    for e in range(E):
-        for i in range(I):
-            r = torch.randperm(H - 1, generator=g)[:3] + 1
-            wu[e, r, i] = torch.randint(0, 2, (3,), generator=g).float() * 2 - 1
+    if mode == "up_dense":
+        wu[:, 1:, :] = torch.randint(-1, 2, (E, H - 1, I), generator=g).float()
+    else:
+        nu = 3 if mode == "mixed" else 1
+        for e in range(E):
+            for i in range(I):
+                r = torch.randperm(H - 1, generator=g)[:nu] + 1
+                wu[e, r, i] = torch.randint(0, 2, (nu,), generator=g).float() * 2 - 1
     wd = torch.zeros(E, I, H)
-    for e in range(E):
-        for j in range(H):
-            r = torch.randperm(I, generator=g)[:2]
-            wd[e, r, j] = torch.randint(0, 2, (2,), generator=g).float() * 2 - 1
+    if mode == "down_dense":
+        wd[:] = torch.randint(-1, 2, (E, I, H), generator=g).float()
+    else:
+        nd = 2 if mode == "mixed" else 1
+        for e in range(E):
+            for j in range(H):
+                r = torch.randperm(I, generator=g)[:nd]
+                wd[e, r, j] = torch.randint(0, 2, (nd,), generator=g).float() * 2 - 1
     logits = torch.randn(T, E, generator=g) - 4.0
     for t in range(T):
         logits[t, torch.randperm(E, generator=g)[:k]] = 1.0   # ties between k distinct experts
     return x, wg, wu, wd, logits
 
 
+def _bf16_exact(a):
+    a = np.asarray(a, dtype=np.float64)
+    return np.array_equal(torch.from_numpy(a).to(torch.bfloat16).double().numpy(), a)
+
+
+@pytest.mark.parametrize("mode,T,tile", [
+    ("mixed", 50, -1), ("up_dense", 50, -1), ("down_dense", 50, -1),
+    ("mixed", 300, 3), ("up_dense", 300, 3), ("down_dense", 300, 3),
+    ("mixed", 300, 4), ("up_dense", 300, 4), ("down_dense", 300, 4)])
 @pytest.mark.parametrize("k", [1, 2])
 @pytest.mark.parametrize("sched", ["static", "dynamic"])
-def test_integer_exact(k, sched):
-    x, wg, wu, wd, logits = _exact_case(k)
+def test_integer_exact(k, sched, mode, T, tile):
+    """Bit-exact layer output on integer experts, through the stream tiles
+    (T = 50: the 64-row variant) and the LDS-ring tiles forced (64 and 128
+    rows: several row blocks per expert and a partial last block)."""
+    x, wg, wu, wd, logits = _exact_case(k, mode, T=T)
     E, H, I = wg.shape[0], wg.shape[1], wg.shape[2]
-    T = x.shape[0]
-    ws = et.Workspace(et.WL_MOE, 64, H, I, E, k, device=DEV)
+    ws = et.Workspace(et.WL_MOE, 512, H, I, E, k, device=DEV)
     out = torch.full((T, H), float("nan"), device=DEV)
     dev = lambda t: t.to(torch.bfloat16).to(DEV)
-    say("moe integer", k, sched)
+    say("moe integer", k, sched, mode, T, tile)
     et.moe_layer(logits.to(DEV), dev(x), synth.k_major(dev(wg)), synth.k_major(dev(wu)),
-                 synth.k_major(dev(wd)), out, ws, sched)
+                 synth.k_major(dev(wd)), out, ws, sched, tile=tile)
     torch.cuda.synchronize()
     assert ws.status()["status"] == 0
     ref = omoe.moe_layer(logits.numpy(), x.numpy(), k, (wg.numpy(), wu.numpy(), wd.numpy()))
@@ -199,10 +244,86 @@ def test_integer_exact(k, sched):
             e = ids[t, s]
             gg = x[t].numpy().astype(np.float64) @ wg[e].numpy()
             uu = x[t].numpy().astype(np.float64) @ wu[e].numpy()
-            exact[t] += w[t, s] * ((gg * uu) @ wd[e].numpy())
+            assert gg.min() >= 16
+            hh = gg * uu
+            yy = hh @ wd[e].numpy()
+            assert _bf16_exact(hh) and _bf16_exact(yy)   # the premise of exactness
+            exact[t] += w[t, s] * yy
     assert np.array_equal(out.cpu().numpy(), exact.astype(np.float32))
     aux = {kk: v.cpu().numpy() for kk, v in et.moe_aux(ws, T).items()}
-    assert np.array_equal(aux["ids"], ids) and np.array_equal(aux["perm"], ref["perm"])
+    check_routing(aux, ref, k, I, T, tile)
+    if mode != "mixed":
+        assert np.abs(exact).max() > 256      # beyond what the narrow case reaches
+
+
+@pytest.mark.parametrize("tile", [3, 4])
+def test_wide_tile_needs_hidden_multiple_of_256(tile):
+    """A forced wide variant on a hidden size its 256-column down tiles do not
+    divide is refused before any launch; the automatic choice falls back to
+    the 64-row stream variant and matches the oracle."""
+    T, E, k, H, I = 300, 4, 2, 384, 256
+    ws = et.Workspace(et.WL_MOE, 512, H, I, E, k, device=DEV)
+    logits = synth.normal_bf16((T, E), 1.0, 5, DEV).float()
+    x = synth.normal_bf16((T, H), 1.0, 6, DEV)
+    wg = synth.normal_bf16((E, H, I), 0.02, 7, DEV)
+    wu = synth.normal_bf16((E, H, I), 0.02, 8, DEV)
+    wd = synth.normal_bf16((E, I, H), 0.02, 9, DEV)
+    out = torch.full((T, H), float("nan"), device=DEV)
+    args = (logits, x, synth.k_major(wg), synth.k_major(wu), synth.k_major(wd), out, ws)
+    with pytest.raises(et.EtError) as err:
+        et.moe_layer(*args, "static", tile=tile)
+    assert err.value.code == et.EUNSUPPORTED
+    say("moe H=384 automatic tile")
+    et.moe_layer(*args, "dynamic")
+    torch.cuda.synchronize()
+    assert ws.status()["status"] == 0
+    ref = omoe.moe_layer(to_np(logits), to_np(x), k, (to_np(wg), to_np(wu), to_np(wd)))
+    aux = {kk: v.cpu().numpy() for kk, v in et.moe_aux(ws, T).items()}
+    check_routing(aux, ref, k, I, T)
+    assert moe_tiling(T, k, hidden=H)[0] == 64
+    assert_rel(out.cpu().numpy(), ref["out"], 1e-2, "out")
+
+
+_TIE_VALUES = np.array([-1.0, -0.0, 0.0, 0.5, 0.5, 1.0], np.float32)
+
+
+@pytest.mark.parametrize("E,k", [(5, 1), (5, 3), (8, 2), (16, 3), (16, 1)])
+@pytest.mark.parametrize("T", [64, 200])
+@pytest.mark.parametrize("sched", SCHEDS)
+def test_routing_ties_and_signed_zeros(E, k, T, sched):
+    """Logits drawn from {-1, -0.0, +0.0, 0.5, 1}: most tokens have ties that
+    straddle the k-th place and zeros of both signs.  The GPU's order-preserving
+    keys must pick exactly the oracle's experts (descending logit, ties to the
+    lower index, -0.0 equal to +0.0), and the grouping built on them must be
+    bit-exact.  T = 200 routes in 25 chunks (broadcast events, chunk 0
+    publishes the scan), T = 64 in 8; E = 5 is not a multiple of 4."""
+    H, I = 256, 256
+    rng = np.random.default_rng(1000 * E + 10 * k + T)
+    L = rng.choice(_TIE_VALUES, size=(T, E)).astype(np.float32)
+    n_tie_k = sum(1 for t in range(T) if k < E and
+                  np.float32(sorted(L[t], reverse=True)[k - 1]) == sorted(L[t], reverse=True)[k])
+    assert n_tie_k >= T // 4                 # the boundary ties are really exercised
+    assert (np.signbit(L) & (L == 0)).any() and ((~np.signbit(L)) & (L == 0)).any()
+    logits = torch.from_numpy(L).to(DEV)
+    x = synth.normal_bf16((T, H), 1.0, 11, DEV)
+    wg = synth.normal_bf16((E, H, I), 0.02, 12, DEV)
+    wu = synth.normal_bf16((E, H, I), 0.02, 13, DEV)
+    wd = synth.normal_bf16((E, I, H), 0.02, 14, DEV)
+    ws = _ws_dims(256, H, I, E, k)
+    out = torch.full((T, H), float("nan"), device=DEV)
+    say("moe routing ties", E, k, T, sched)
+    et.moe_layer(logits, x, synth.k_major(wg), synth.k_major(wu), synth.k_major(wd), out, ws, sched)
+    torch.cuda.synchronize()
+    assert ws.status()["status"] == 0
+    ref = omoe.moe_layer(L, to_np(x), k, (to_np(wg), to_np(wu), to_np(wd)))
+    aux = {kk: v.cpu().numpy() for kk, v in et.moe_aux(ws, T).items()}
+    check_routing(aux, ref, k, I, T)
+    assert_rel(out.cpu().numpy(), ref["out"], 1e-2, "out")
+
+
+@functools.lru_cache(maxsize=4)
+def _ws_dims(max_tokens, H, I, E, k):
+    return et.Workspace(et.WL_MOE, max_tokens, H, I, E, k, device=DEV)
 
 
 def test_symbolic_token_counts_one_workspace():

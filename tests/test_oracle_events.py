@@ -124,3 +124,44 @@ def test_list_out_of_topological_order_deadlocks():
     g.tasks.remove("gemm2")
     with pytest.raises(ev.Deadlock):
         ev.run_static(g, [["rs", "gemm0", "gemm1"]], _dur)
+
+
+@pytest.mark.parametrize("batch,rows,gate_cols,h_tile,down_cols,k_slices", [
+    (1, 16, 16, 128, 16, 1), (64, 16, 16, 128, 16, 1), (40, 32, 32, 128, 64, 2),
+    (17, 64, 64, 256, 128, 4), (100, 16, 128, 128, 32, 3)])
+def test_mlp_table_brute_force(batch, rows, gate_cols, h_tile, down_cols, k_slices):
+    """Enumerate every task of the dense MLP chain under a tiling and count
+    the notifies each event receives: gate/up tile (m, n) covers h columns
+    [n*gate_cols, (n+1)*gate_cols) of row block m and notifies the E_h[m, c]
+    of the h tile holding them; down tile (m, n2, s) covers K-slice s of the
+    output columns of tile n2 and, with several K-slices, notifies E_y[m, n2].
+    The table's task counts and wait counts must equal the enumeration."""
+    hidden, inter = 512, 768
+    tab = ev.mlp_table(batch, hidden, inter, rows, gate_cols, h_tile, down_cols, k_slices)
+    mb = -(-batch // rows)
+    gate = [(m, n) for m in range(mb) for n in range(inter // gate_cols)]
+    down = [(m, n2, s) for m in range(mb) for n2 in range(hidden // down_cols)
+            for s in range(k_slices)]
+    assert tab["tasks"]["gate_up"] == len(gate)
+    assert tab["tasks"]["down"] == len(down)
+    # every h column is produced by exactly one gate/up tile
+    cols = sorted(c for (m, n) in gate if m == 0 for c in range(n * gate_cols, (n + 1) * gate_cols))
+    assert cols == list(range(inter))
+    eh = ev.notify_counts([(t, (t[0], t[1] * gate_cols // h_tile)) for t in gate],
+                          (mb, inter // h_tile))
+    assert tab["events"]["E_h"]["shape"] == (mb, inter // h_tile)
+    assert (tab["events"]["E_h"]["wait_count"] == eh).all()
+    if k_slices > 1:
+        ey = ev.notify_counts([(t, (t[0], t[1])) for t in down], (mb, hidden // down_cols))
+        assert (tab["events"]["E_y"]["wait_count"] == ey).all()
+        assert tab["tasks"]["reduce"] == mb * (hidden // down_cols)
+    else:
+        assert "E_y" not in tab["events"] and tab["tasks"]["reduce"] == 0
+
+
+def test_mlp_table_symbolic_batch():
+    """One event table shape per row-block count: the E_h shape grows with
+    ceil(B / rows) and nothing else (the symbolic batch dimension)."""
+    shapes = {B: ev.mlp_table(B, 2048, 5632, 16, 16, 128, 16, 1)["events"]["E_h"]["shape"]
+              for B in (1, 4, 16, 17, 64)}
+    assert shapes == {1: (1, 44), 4: (1, 44), 16: (1, 44), 17: (2, 44), 64: (4, 44)}
