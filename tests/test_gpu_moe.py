@@ -43,7 +43,7 @@ def _oracle(name, T):
     return omoe.moe_layer(to_np(logits), to_np(x), cfg["top_k"], moe_oracle_weights(wg, wu, wd))
 
 
-def check_routing(aux, ref, k, inter, T, tile=-1):
+def check_routing(aux, ref, k, inter, T, tile=-1, hidden=2048):
     """Integer outputs bit-exact (ids, counts, CSR offsets of rows and of the
     gate/up tasks of the tiling the call used, the permutation and its
     inverse); routing weights within 1e-5 of the largest."""
@@ -52,7 +52,7 @@ def check_routing(aux, ref, k, inter, T, tile=-1):
     assert np.array_equal(aux["tok_indptr"], ref["tok_indptr"]), "tok_indptr"
     assert np.array_equal(aux["perm"], ref["perm"]), "perm"
     assert np.array_equal(aux["inv"], ref["inv"]), "inv"
-    rows, bn1, _ = moe_tiling(T, k, tile)
+    rows, bn1, _ = moe_tiling(T, k, tile, hidden)
     assert np.array_equal(aux["task_indptr"], omoe.task_indptr(ref["counts"], rows, inter // bn1)), \
         "task_indptr"
     assert np.abs(aux["w"] - ref["w"]).max() <= 1e-5 * np.abs(ref["w"]).max(), "topk_w"
@@ -61,7 +61,7 @@ def check_routing(aux, ref, k, inter, T, tile=-1):
 def check_against_oracle(name, T, out, aux, tile=-1):
     cfg = synth.MOE_PRESETS[name]
     ref = _oracle(name, T)
-    check_routing(aux, ref, cfg["top_k"], cfg["inter"], T, tile)
+    check_routing(aux, ref, cfg["top_k"], cfg["inter"], T, tile, cfg["hidden"])
     assert_rel(out, ref["out"], 1e-2, "out")
     return ref
 
@@ -251,7 +251,7 @@ def test_integer_exact(k, sched, mode, T, tile):
             exact[t] += w[t, s] * yy
     assert np.array_equal(out.cpu().numpy(), exact.astype(np.float32))
     aux = {kk: v.cpu().numpy() for kk, v in et.moe_aux(ws, T).items()}
-    check_routing(aux, ref, k, I, T, tile)
+    check_routing(aux, ref, k, I, T, tile, hidden=H)
     if mode != "mixed":
         assert np.abs(exact).max() > 256      # beyond what the narrow case reaches
 
@@ -279,8 +279,8 @@ def test_wide_tile_needs_hidden_multiple_of_256(tile):
     assert ws.status()["status"] == 0
     ref = omoe.moe_layer(to_np(logits), to_np(x), k, (to_np(wg), to_np(wu), to_np(wd)))
     aux = {kk: v.cpu().numpy() for kk, v in et.moe_aux(ws, T).items()}
-    check_routing(aux, ref, k, I, T)
-    assert moe_tiling(T, k, hidden=H)[0] == 64
+    check_routing(aux, ref, k, I, T, hidden=H)
+    assert moe_tiling(T, k, hidden=H)[:2] == (64, 16)
     assert_rel(out.cpu().numpy(), ref["out"], 1e-2, "out")
 
 
@@ -317,7 +317,7 @@ def test_routing_ties_and_signed_zeros(E, k, T, sched):
     assert ws.status()["status"] == 0
     ref = omoe.moe_layer(L, to_np(x), k, (to_np(wg), to_np(wu), to_np(wd)))
     aux = {kk: v.cpu().numpy() for kk, v in et.moe_aux(ws, T).items()}
-    check_routing(aux, ref, k, I, T)
+    check_routing(aux, ref, k, I, T, hidden=H)
     assert_rel(out.cpu().numpy(), ref["out"], 1e-2, "out")
 
 
