@@ -3,6 +3,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/et.h"
 #include "et_device.hpp"
@@ -88,6 +89,43 @@ int fill_common(LaunchCommon& lc, void* ws, const et_plan* plan, int sched, cons
   if (lc.shards != 1 && lc.shards != kMaxShards) return ET_EINVAL;
   lc.stream = stream;
   return workers_for_current_device(&lc.G);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Library-held scratch of the allocation-free MoE entry point: the workspace
+// (header, counter banks, ready queue, intermediates) of callers that cannot
+// allocate device memory.  One copy per device, held until the process ends.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(64) << 20;
+
+}  // namespace et
+
+static __device__ __align__(256) unsigned char scratch[et::kScratchBytes];
+
+namespace et {
+namespace {
+
+struct ScratchState {
+  void* ptr = nullptr;   // device address of `scratch` on this device
+  et_plan plan{};        // plan the scratch is laid out for (bytes == 0: none yet)
+};
+std::mutex g_scratch_mu;
+ScratchState g_scratch[64];
+
+// Address of this device's copy of `scratch`, looked up once per device with
+// that device current (the array's name is only a host-side stand-in).
+int scratch_for_device(int dev, ScratchState** out) {
+  ScratchState& st = g_scratch[dev];
+  if (!st.ptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ET_EHIP;
+    if ((reinterpret_cast<uintptr_t>(p) & 255) != 0) return ET_EHIP;
+    st.ptr = p;
+  }
+  *out = &st;
+  return ET_OK;
 }
 
 }  // namespace
@@ -264,6 +302,50 @@ int et_read_status(const void* ws, const et_plan* plan, hipStream_t stream, et_r
   }
   out->last_extent = h[HDR_EXT0 + (1 - (h[HDR_BANK] & 1))];
   return ET_OK;
+}
+
+int et_moe_layer_noalloc(const float* logits, const uint16_t* x, int n_tokens, int hidden,
+                         int inter, int n_experts, int top_k, const uint16_t* w_gate,
+                         const uint16_t* w_up, const uint16_t* w_down, float* out, int sched,
+                         const et_opts* opts, hipStream_t stream) {
+  if (n_tokens < 0) return ET_EINVAL;
+  if (n_tokens == 0) return ET_OK;
+  if (!logits || !x || !w_gate || !w_up || !w_down || !out) return ET_EINVAL;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return ET_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchState* st = nullptr;
+  int e = scratch_for_device(dev, &st);
+  if (e) return e;
+  const et_plan& cur = st->plan;
+  const bool same_dims = cur.bytes != 0 && cur.hidden == hidden && cur.inter == inter &&
+                         cur.n_experts == n_experts && cur.top_k == top_k;
+  bool init = (opts && (opts->debug_flags & ET_SCRATCH_RESET)) != 0;
+  if (!same_dims || n_tokens > cur.max_tokens) {
+    // lay the scratch out for a power-of-two token bound (at least 16), so
+    // that nearby token counts reuse the layout; fall back to the exact count
+    // when the rounded plan does not fit
+    int bound = 16;
+    while (bound < n_tokens) bound *= 2;
+    if (same_dims && cur.max_tokens > bound) bound = cur.max_tokens;
+    et_plan p;
+    e = et_plan_workspace(ET_WL_MOE, bound, hidden, inter, n_experts, top_k, &p);
+    if (e == ET_OK && p.bytes > kScratchBytes)
+      e = et_plan_workspace(ET_WL_MOE, n_tokens, hidden, inter, n_experts, top_k, &p);
+    if (e) return e;
+    if (p.bytes > kScratchBytes) return ET_EWORKSPACE;
+    st->plan = p;
+    init = true;
+  }
+  if (init) {
+    // header, counter banks, queue and run counts start cleared (a kernel,
+    // not a memset node, so the call can also be captured in a graph)
+    hipLaunchKernelGGL(ws_init_kernel, dim3(256), dim3(256), 0, stream,
+                       static_cast<int*>(st->ptr), st->plan.off_aux / 4, st->plan.workload);
+    if (hipGetLastError() != hipSuccess) return ET_EHIP;
+  }
+  return et_moe_layer(logits, x, n_tokens, w_gate, w_up, w_down, out, st->ptr, &st->plan, sched,
+                      opts, stream);
 }
 
 const char* et_status_str(int s) {

@@ -20,7 +20,7 @@ SCHED_STATIC, SCHED_DYNAMIC, SCHED_BARRIER, SCHED_PER_OP = 0, 1, 2, 3
 SCHEDS = {"static": 0, "dynamic": 1, "barrier": 2, "per_op": 3}
 OK, EINVAL, EWORKSPACE, EHIP, ETIMEOUT, EUNSUPPORTED, ESTATE = range(7)
 WL_SPLITK, WL_MLP, WL_MOE = 1, 2, 3
-DEBUG_COUNTS, DEBUG_TRACE = 1, 2
+DEBUG_COUNTS, DEBUG_TRACE, SCRATCH_RESET = 1, 2, 4
 
 c_int, c_size_t, c_void_p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 
@@ -80,13 +80,16 @@ def lib():
                              P(Plan), c_int, P(Opts), c_void_p]
         L.et_moe_layer.argtypes = [c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_void_p, P(Plan), c_int, P(Opts), c_void_p]
+        L.et_moe_layer_noalloc.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                           c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                           P(Opts), c_void_p]
         L.et_read_status.argtypes = [c_void_p, P(Plan), c_void_p, P(Report)]
         L.et_status_str.argtypes = [c_int]
         L.et_status_str.restype = ctypes.c_char_p
         L.et_num_workers.argtypes = []
         for f in ("et_plan_workspace", "et_workspace_init", "et_workspace_layout",
-                  "et_splitk_reduce", "et_mlp", "et_moe_layer", "et_read_status",
-                  "et_num_workers"):
+                  "et_splitk_reduce", "et_mlp", "et_moe_layer", "et_moe_layer_noalloc",
+                  "et_read_status", "et_num_workers"):
             getattr(L, f).restype = c_int
         _lib = L
     return _lib
@@ -243,6 +246,24 @@ def moe_layer(logits, x, w_gate, w_up, w_down, out, ws, sched="dynamic", stream=
     o = _opts(**opts)
     _check(lib().et_moe_layer(*args, ws.ptr, ctypes.byref(ws.plan), SCHEDS.get(sched, sched),
                               ctypes.byref(o), _stream(stream)), "et_moe_layer")
+
+
+def moe_layer_noalloc(logits, x, w_gate, w_up, w_down, out, sched="dynamic", stream=None,
+                      **opts):
+    """The allocation-free entry point: same tensors as moe_layer, no
+    workspace (the library holds a fixed 64 MiB scratch array per device)."""
+    T, E = logits.shape
+    H = x.shape[1]
+    I = w_gate.shape[1]
+    k = opts.pop("top_k")
+    args = (_ptr(logits, torch.float32, "logits", (T, E)), _ptr(x, torch.bfloat16, "x", (T, H)),
+            T, H, I, E, k, _ptr(w_gate, torch.bfloat16, "w_gate", (E, I, H)),
+            _ptr(w_up, torch.bfloat16, "w_up", (E, I, H)),
+            _ptr(w_down, torch.bfloat16, "w_down", (E, H, I)),
+            _ptr(out, torch.float32, "out", (T, H)))
+    o = _opts(**opts)
+    _check(lib().et_moe_layer_noalloc(*args, SCHEDS.get(sched, sched), ctypes.byref(o),
+                                      _stream(stream)), "et_moe_layer_noalloc")
 
 
 def moe_aux(ws, T, intermediates=False):

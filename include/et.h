@@ -74,7 +74,9 @@ enum { ET_WL_SPLITK = 1, ET_WL_MLP = 2, ET_WL_MOE = 3 };
 /* Debug flags. */
 enum {
   ET_DEBUG_COUNTS = 1,  /* count how many times each task ran (et_layout.runs) */
-  ET_DEBUG_TRACE = 2    /* record each task's workgroup and start / end time (et_layout.trace) */
+  ET_DEBUG_TRACE = 2,   /* record each task's workgroup and start / end time (et_layout.trace) */
+  ET_SCRATCH_RESET = 4  /* et_moe_layer_noalloc only: clear the library-held scratch state (event
+                           counters, ready queue, sticky fault word) before this call */
 };
 
 /* Launch modes of the persistent kernels.  Every workgroup of a persistent
@@ -215,6 +217,29 @@ int et_moe_layer(const float* logits, const uint16_t* x, int n_tokens,
                  const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                  float* out, void* ws, const et_plan* plan, int sched,
                  const et_opts* opts, hipStream_t stream);
+
+/* Allocation-free variant of et_moe_layer, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and results as et_moe_layer, with the layer's
+ * dimensions passed directly instead of a workspace: the workspace is a fixed
+ * 64 MiB array of device memory held by the library, one copy per device for the
+ * life of the process, so the call itself allocates nothing (no hipMalloc, no
+ * allocating library routine).  The call lays that array out for the given
+ * dimensions and a power-of-two token bound; when the dimensions change or the
+ * token count outgrows the bound it re-plans and clears the array's state with a
+ * kernel on `stream`.  A layer whose workspace would exceed 64 MiB returns
+ * ET_EWORKSPACE and enqueues nothing (64 MiB holds e.g. 1024 tokens of a layer with
+ * hidden 2048, 128 experts, top-8, intermediate 768, or 256 tokens of hidden 7168,
+ * 256 experts, top-8, intermediate 2048).  Every call on one device shares its
+ * array and leaves its contents (routing tensors, intermediates) behind for the
+ * next: calls that can overlap in time on one device (two streams) race and must
+ * not be issued.  A device fault recorded in the array is sticky, as in a
+ * workspace, until a call passes ET_SCRATCH_RESET in opts->debug_flags or
+ * re-plans. */
+int et_moe_layer_noalloc(const float* logits, const uint16_t* x, int n_tokens, int hidden,
+                         int inter, int n_experts, int top_k, const uint16_t* w_gate,
+                         const uint16_t* w_up, const uint16_t* w_down, float* out, int sched,
+                         const et_opts* opts, hipStream_t stream);
 
 /* Waits for `stream`, then reads the workspace's device state. */
 int et_read_status(const void* ws, const et_plan* plan, hipStream_t stream, et_report* out);
