@@ -734,6 +734,9 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       if ((sched == ET_SCHED_STATIC || sched == ET_SCHED_BARRIER) && !seen_group) {
         if (!wg_wait_bcast(c, EV_GROUP, EV_GROUP, task)) return false;
         seen_group = true;
+      } else if (sched == ET_SCHED_DYNAMIC &&
+                 !wg_wait(c, m.ev_exp + e, c_tok[e + 1] - c_tok[e], task)) {
+        return false;   // early-pushed: the expert's rows must be grouped
       }
       for (int i = tid; i < rows; i += kThreads) {
         const int pos = pos0 + i;
@@ -1014,6 +1017,45 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
           t0_notify_bcast(c, EV_SCAN, EV_SCAN, 1, 1, NR);
         }
       }
+      if (sched == ET_SCHED_DYNAMIC) {
+        // Early push (the appendix of the dynamic schedule: consumers are
+        // queued before their producers finish and wait on their event
+        // before they run): once the scan knows every expert's row blocks,
+        // the routing chunks together push all gate/up tasks, chunk r an
+        // equal share of them, before any chunk has grouped its tokens.  A
+        // gate/up task streams its weights and then waits on its expert's
+        // E_exp event, so the weight stream overlaps the grouping.  The
+        // pushed tasks read the offsets and totals chunk 0 publishes before
+        // EV_SCAN (few chunks: this chunk published them itself).
+        if (task == 0) set_total(c, nb * (nt1 + nt2) + ncomb);
+        wg_release();
+        if (task != 0 && many_chunks && !wg_wait_bcast(c, EV_SCAN, EV_SCAN, task)) return false;
+        const int* blk = reinterpret_cast<const int*>(s1) + 1024;   // exclusive block offsets
+        const int total1 = nb * nt1;
+        const int j0 = (int)((long long)task * total1 / NR);
+        const int j1 = (int)((long long)(task + 1) * total1 / NR);
+        // gate/up task j of the push order (experts ascending, block-major
+        // within an expert) -> expert holding it: the largest e whose first
+        // task is <= j (experts without rows share their successor's start)
+        auto expert_of = [&](int j) ET_INLINE {
+          int lo = 0, hi = m.E;
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (blk[mid] * nt1 <= j) lo = mid; else hi = mid;
+          }
+          return lo;
+        };
+        auto nblk_of = [&](int e) ET_INLINE { return (e + 1 < m.E ? blk[e + 1] : nb) - blk[e]; };
+        wg_push(c, j1 - j0,
+                [&](int i) {
+                  const int j = j0 + i, e = expert_of(j), l = j - blk[e] * nt1;
+                  return base1 + blk[e] * nt1 + (l % nt1) * nblk_of(e) + l / nt1;
+                },
+                [&](int i) {
+                  const int j = j0 + i, e = expert_of(j);
+                  return tile_key(e, (j - blk[e] * nt1) % nt1, nt1);
+                });
+      }
       ts = trace_now(c);
       group_chunk(task);
       count_run(c, NR + 1 + task);
@@ -1024,54 +1066,19 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
         return true;
       }
       // dynamic: data-dependent notify targets -- the experts this chunk's
-      // tokens chose, each decremented by this chunk's rows for it; the
-      // experts whose events this completes have all their gate/up tiles
-      // pushed in one piece (block-major within each expert)
-      if (task == 0) set_total(c, nb * (nt1 + nt2) + ncomb);
+      // tokens chose, each decremented by this chunk's rows for it (wait
+      // count: the rows routed to the expert); their gate/up tasks wait on it
       const int* cur = s_i;
       const int* base = s_i + 1024;
-      int* fe = s_i + 2048;     // fired experts
-      int* fpre = s_i + 3072;   // their gate/up task counts -> exclusive prefix
       const int* tokp = reinterpret_cast<const int*>(s1);
-      const int* blk = tokp + 1024;
-      if (tid == 0) sh.v[6] = 0;
-      __syncthreads();
       for (int e = tid; e < m.E; e += kThreads) {
         const int n = cur[e] - base[e];
         if (n > 0) {
           const int wcnt = (e + 1 < m.E ? tokp[e + 1] : m.T * m.k) - tokp[e];
           const int old = add_rlx(c.ev + m.ev_exp + e, -n);
-          if (old - n == -wcnt) fe[atomicAdd(&sh.v[6], 1)] = e;
-          else if (old - n < -wcnt) raise_fault(ra, ET_ESTATE, task, m.ev_exp + e, old - n);
+          if (old - n < -wcnt) raise_fault(ra, ET_ESTATE, task, m.ev_exp + e, old - n);
         }
       }
-      __syncthreads();
-      const int nf = sh.v[6];
-      if (nf == 0) return true;
-      // the pushed tasks read the offsets chunk 0 publishes before EV_SCAN
-      // (few chunks: this chunk published them itself)
-      if (task != 0 && many_chunks && !wg_wait_bcast(c, EV_SCAN, EV_SCAN, task)) return false;
-      auto nblk_of = [&](int e) ET_INLINE { return (e + 1 < m.E ? blk[e + 1] : nb) - blk[e]; };
-      for (int i = tid; i < nf; i += kThreads) fpre[i] = nblk_of(fe[i]) * nt1;
-      __syncthreads();
-      const int ntask = block_exscan(fpre, nf, reinterpret_cast<int*>(s1) + 2048);
-      auto slot_of = [&](int i) ET_INLINE {   // fired expert holding task i
-        int lo = 0, hi = nf;
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (fpre[mid] <= i) lo = mid; else hi = mid;
-        }
-        return lo;
-      };
-      wg_push(c, ntask,
-              [&](int i) {
-                const int j = slot_of(i), e = fe[j], l = i - fpre[j];
-                return base1 + blk[e] * nt1 + (l % nt1) * nblk_of(e) + l / nt1;
-              },
-              [&](int i) {
-                const int j = slot_of(i);
-                return tile_key(fe[j], (i - fpre[j]) % nt1, nt1);
-              });
       return true;
     }
     if (task == NR) {   // the scan as a task of its own: barrier and per-op modes
