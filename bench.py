@@ -188,6 +188,56 @@ def traffic_summary(fetch_db, write_db, key):
     print(json.dumps({key: ent}, indent=1))
 
 
+def ceilings():
+    """Sustained rates of this device next to its published peaks: the
+    library's MFMA-only loop and streaming-read kernels, a device copy, and
+    hipBLASLt bf16 GEMMs (torch.matmul) of the large layer's gate/up shape
+    and a square one.  Printed as one JSON object."""
+    import torch
+    from event_driven_moe_amd import et
+    G = et.num_workers()
+    res = {"device": torch.cuda.get_device_name(0), "compute_units": G}
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3   # seconds per call
+
+    out = torch.zeros(G * 4, device="cuda")
+    iters = 25000
+    t = timed(lambda: et.ceiling_mfma(out, iters), 5)
+    tf = G * 4 * iters * 32 * 16384 / t / 1e12
+    res["mfma_only_bf16"] = {"tflops": round(tf, 1), "frac_of_published": round(tf / MFMA_BF16_PEAK_TFS, 4),
+                             "ms": round(t * 1e3, 3)}
+    buf = torch.empty(8 << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    for wpc in (2, 4, 8):
+        o = torch.zeros(G * wpc * 4, dtype=torch.int32, device="cuda")
+        t = timed(lambda: et.ceiling_stream(buf, o, wpc), 5)
+        res["stream_read_%dwg_per_cu" % wpc] = {"gbs": round(buf.numel() / t / 1e9, 1),
+                                                "frac_of_published": round(buf.numel() / t / 1e9 / HBM_PEAK_GBS, 4)}
+    half = buf[: 4 << 30]
+    dst = torch.empty_like(half)
+    t = timed(lambda: dst.copy_(half), 5)
+    res["device_copy"] = {"gbs_read_plus_write": round(2 * half.numel() / t / 1e9, 1)}
+    del buf, dst, half
+    for M, N, K in ((8192, 4096, 7168), (8192, 8192, 8192)):
+        a = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+        b = torch.randn(K, N, device="cuda").to(torch.bfloat16)
+        t = timed(lambda: torch.matmul(a, b), 20)
+        tf = 2 * M * N * K / t / 1e12
+        res["hipblaslt_bf16_%dx%dx%d" % (M, N, K)] = {"tflops": round(tf, 1),
+                                                       "frac_of_published": round(tf / MFMA_BF16_PEAK_TFS, 4)}
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +255,8 @@ def main():
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="no GPU work: read two rocprofv3 --pmc databases (FETCH_SIZE, "
                          "WRITE_SIZE) of this command and record the MoE kernel's HBM bytes")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="measure the device's sustained MFMA and HBM rates instead of the layer")
     ap.add_argument("--kernel-stats", metavar="DB",
                     help="no GPU work: print per-kernel statistics of a rocprofv3 --kernel-trace database")
     args = ap.parse_args()
@@ -214,6 +266,9 @@ def main():
     if args.traffic:
         traffic_summary(args.traffic[0], args.traffic[1],
                         "%s:T%d:%s" % (args.workload, args.tokens, args.sched))
+        return
+    if args.ceilings:
+        ceilings()
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "

@@ -83,13 +83,15 @@ def lib():
         L.et_moe_layer_noalloc.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                                            c_void_p, c_void_p, c_void_p, c_void_p, c_int,
                                            P(Opts), c_void_p]
+        L.et_ceiling_mfma.argtypes = [c_void_p, c_int, c_void_p]
+        L.et_ceiling_stream.argtypes = [c_void_p, c_size_t, c_void_p, c_int, c_void_p]
         L.et_read_status.argtypes = [c_void_p, P(Plan), c_void_p, P(Report)]
         L.et_status_str.argtypes = [c_int]
         L.et_status_str.restype = ctypes.c_char_p
         L.et_num_workers.argtypes = []
         for f in ("et_plan_workspace", "et_workspace_init", "et_workspace_layout",
                   "et_splitk_reduce", "et_mlp", "et_moe_layer", "et_moe_layer_noalloc",
-                  "et_read_status", "et_num_workers"):
+                  "et_read_status", "et_num_workers", "et_ceiling_mfma", "et_ceiling_stream"):
             getattr(L, f).restype = c_int
         _lib = L
     return _lib
@@ -285,6 +287,22 @@ def moe_aux(ws, T, intermediates=False):
         aux["h"] = ws.view(lay.h, torch.bfloat16, T * k * ws.plan.inter).view(T * k, ws.plan.inter)
         aux["y"] = ws.view(lay.y, torch.bfloat16, T * k * ws.plan.hidden).view(T * k, ws.plan.hidden)
     return aux
+
+
+def ceiling_mfma(out, iters, stream=None):
+    """Enqueues the MFMA-only microbenchmark (out: float32 [G*4] device tensor)."""
+    _check(lib().et_ceiling_mfma(_ptr(out, torch.float32, "out"), iters, _stream(stream)),
+           "et_ceiling_mfma")
+
+
+def ceiling_stream(src, out, wgs_per_cu=4, stream=None):
+    """Enqueues the streaming-read microbenchmark over the bytes of ``src``
+    (out: int32 [G*wgs_per_cu*4] device tensor)."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    _check(lib().et_ceiling_stream(c_void_p(src.data_ptr()), src.numel() * src.element_size(),
+                                   _ptr(out, torch.int32, "out"), wgs_per_cu, _stream(stream)),
+           "et_ceiling_stream")
 
 
 def num_workers():

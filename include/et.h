@@ -241,6 +241,21 @@ int et_moe_layer_noalloc(const float* logits, const uint16_t* x, int n_tokens, i
                          const uint16_t* w_up, const uint16_t* w_down, float* out, int sched,
                          const et_opts* opts, hipStream_t stream);
 
+/* Roofline ceilings of the current device (measurement helpers; no workload uses them).
+ * et_ceiling_mfma: one workgroup of four waves per compute unit, each wave issuing
+ *   `iters` blocks of 32 bf16 MFMAs (v_mfma_f32_16x16x32_bf16, 16384 flops each; 8
+ *   independent accumulator chains) on register operands, no memory traffic:
+ *   flops = G * 4 * iters * 32 * 16384 for G = et_num_workers().  out: float [G * 4] (one value per wave, keeps the
+ *   results live).  Timing the launch gives the sustained bf16 MFMA rate.
+ * et_ceiling_stream: reads `bytes` (a multiple of 16; src 16-byte aligned) with
+ *   16-byte loads in a grid-stride loop, G * wgs_per_cu workgroups (1..16 per
+ *   compute unit).  out: int [G * wgs_per_cu * 4].  Timing it on a buffer far larger
+ *   than the caches gives the sustained HBM read rate.
+ * Both enqueue one kernel on `stream` and return ET_OK, ET_EINVAL or ET_EHIP. */
+int et_ceiling_mfma(float* out, int iters, hipStream_t stream);
+int et_ceiling_stream(const void* src, size_t bytes, int* out, int wgs_per_cu,
+                      hipStream_t stream);
+
 /* Waits for `stream`, then reads the workspace's device state. */
 int et_read_status(const void* ws, const et_plan* plan, hipStream_t stream, et_report* out);
 
