@@ -91,6 +91,39 @@ int fill_common(LaunchCommon& lc, void* ws, const et_plan* plan, int sched, cons
   return workers_for_current_device(&lc.G);
 }
 
+// Byte offsets of the common regions (header, counters, queue, debug) and the
+// total, once n_events, max_tasks and the aux bytes are known.
+void finish_plan(et_plan* plan, size_t aux) {
+  size_t o = kHdrBytes;
+  plan->off_counters = o;
+  o = align_up(o + (size_t)2 * plan->n_events * 4, 256);
+  plan->off_slots = o;
+  o = align_up(o + kQCtlBytes + (size_t)kMaxShards * plan->max_tasks * 4, 256);
+  plan->off_runs = o;
+  o = align_up(o + (size_t)plan->max_tasks * 4, 256);
+  plan->off_trace = o;
+  o = align_up(o + (size_t)plan->max_tasks * 16 + 1024 * 8, 256);
+  plan->off_aux = o;
+  plan->aux_bytes = aux;
+  plan->bytes = align_up(o + aux, 256);
+}
+
+// MoE dimension checks shared by the MoE layer and the chain.
+int check_moe_dims(int max_tokens, int hidden, int inter, int n_experts, int top_k) {
+  if (hidden <= 0 || inter <= 0 || n_experts <= 0 || top_k <= 0) return ET_EINVAL;
+  if (top_k > n_experts) return ET_EINVAL;
+  if (hidden % 128 || inter % 128) return ET_EUNSUPPORTED;
+  if (n_experts > kMaxExperts || top_k > kMaxTopK) return ET_EUNSUPPORTED;
+  const size_t tk = (size_t)max_tokens * top_k;
+  if (tk * inter * 2 >= (1ull << 31) || (size_t)max_tokens * hidden * 2 >= (1ull << 31) ||
+      (size_t)inter * hidden * 2 >= (1ull << 31) || tk * hidden * 4 >= (1ull << 31))
+    return ET_EUNSUPPORTED;
+  MoePlan p{max_tokens, hidden, inter, n_experts, top_k, moe_n_route(n_experts)};
+  if ((size_t)p.n_events_max() >= (1ull << 30) || (size_t)p.max_tasks() >= (1ull << 30))
+    return ET_EUNSUPPORTED;
+  return ET_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -164,17 +197,9 @@ int et_plan_workspace(int workload, int max_tokens, int hidden, int inter, int n
     plan->max_tasks = p.max_tasks();
     aux = (size_t)max_tokens * inter * 2;
   } else if (workload == ET_WL_MOE) {
-    if (hidden <= 0 || inter <= 0 || n_experts <= 0 || top_k <= 0) return ET_EINVAL;
-    if (top_k > n_experts) return ET_EINVAL;
-    if (hidden % 128 || inter % 128) return ET_EUNSUPPORTED;
-    if (n_experts > kMaxExperts || top_k > kMaxTopK) return ET_EUNSUPPORTED;
-    const size_t tk = (size_t)max_tokens * top_k;
-    if (tk * inter * 2 >= (1ull << 31) || (size_t)max_tokens * hidden * 2 >= (1ull << 31) ||
-        (size_t)inter * hidden * 2 >= (1ull << 31) || tk * hidden * 4 >= (1ull << 31))
-      return ET_EUNSUPPORTED;
+    const int e = check_moe_dims(max_tokens, hidden, inter, n_experts, top_k);
+    if (e) return e;
     MoePlan p{max_tokens, hidden, inter, n_experts, top_k, moe_n_route(n_experts)};
-    if ((size_t)p.n_events_max() >= (1ull << 30) || (size_t)p.max_tasks() >= (1ull << 30))
-      return ET_EUNSUPPORTED;
     plan->hidden = hidden;
     plan->inter = inter;
     plan->n_experts = n_experts;
@@ -185,18 +210,36 @@ int et_plan_workspace(int workload, int max_tokens, int hidden, int inter, int n
   } else {
     return ET_EINVAL;
   }
-  size_t o = kHdrBytes;
-  plan->off_counters = o;
-  o = align_up(o + (size_t)2 * plan->n_events * 4, 256);
-  plan->off_slots = o;
-  o = align_up(o + kQCtlBytes + (size_t)kMaxShards * plan->max_tasks * 4, 256);
-  plan->off_runs = o;
-  o = align_up(o + (size_t)plan->max_tasks * 4, 256);
-  plan->off_trace = o;
-  o = align_up(o + (size_t)plan->max_tasks * 16 + 1024 * 8, 256);
-  plan->off_aux = o;
-  plan->aux_bytes = aux;
-  plan->bytes = align_up(o + aux, 256);
+  finish_plan(plan, aux);
+  return ET_OK;
+}
+
+int et_plan_block(int max_tokens, int hidden, int inter, int n_experts, int top_k, int mlp_inter,
+                  et_plan* plan) {
+  if (!plan) return ET_EINVAL;
+  std::memset(plan, 0, sizeof(*plan));
+  if (max_tokens <= 0 || mlp_inter <= 0) return ET_EINVAL;
+  int e = check_moe_dims(max_tokens, hidden, inter, n_experts, top_k);
+  if (e) return e;
+  if (mlp_inter % 128) return ET_EUNSUPPORTED;
+  if ((size_t)mlp_inter * hidden * 2 >= (1ull << 31) ||
+      (size_t)max_tokens * mlp_inter * 2 >= (1ull << 31) ||
+      (size_t)max_tokens * n_experts * 4 >= (1ull << 31))
+    return ET_EUNSUPPORTED;
+  const BlockPlan p{MoePlan{max_tokens, hidden, inter, n_experts, top_k, moe_n_route(n_experts)},
+                    mlp_inter};
+  if ((size_t)p.n_events_max() >= (1ull << 30) || (size_t)p.max_tasks() >= (1ull << 30))
+    return ET_EUNSUPPORTED;
+  plan->workload = ET_WL_BLOCK;
+  plan->max_tokens = max_tokens;
+  plan->hidden = hidden;
+  plan->inter = inter;
+  plan->n_experts = n_experts;
+  plan->top_k = top_k;
+  plan->mlp_inter = mlp_inter;
+  plan->n_events = p.n_events_max();
+  plan->max_tasks = p.max_tasks();
+  finish_plan(plan, block_aux_layout(p).bytes);
   return ET_OK;
 }
 
@@ -219,11 +262,17 @@ int et_workspace_layout(const et_plan* plan, int n_tokens, et_layout* out) {
   out->trace = plan->off_trace;
   if (plan->workload == ET_WL_MLP) {
     out->h = plan->off_aux;
-  } else if (plan->workload == ET_WL_MOE) {
+  } else if (plan->workload == ET_WL_MOE || plan->workload == ET_WL_BLOCK) {
     MoePlan p{plan->max_tokens, plan->hidden, plan->inter, plan->n_experts, plan->top_k,
               moe_n_route(plan->n_experts)};
     const MoeAux a = moe_aux_layout(p);
     const size_t b = plan->off_aux;
+    if (plan->workload == ET_WL_BLOCK) {
+      const BlockAux ba = block_aux_layout(BlockPlan{p, plan->mlp_inter});
+      out->logits = b + ba.logits;
+      out->z = b + ba.zb;
+      out->h2 = b + ba.h2;
+    }
     out->topk_ids = b + a.topk_ids;
     out->topk_w = b + a.topk_w;
     out->counts = b + a.counts;
@@ -274,6 +323,24 @@ int et_moe_layer(const float* logits, const uint16_t* x, int n_tokens, const uin
   if (n_tokens == 0) return ET_OK;
   if (!logits || !x || !w_gate || !w_up || !w_down || !out) return ET_EINVAL;
   return launch_moe(lc, logits, x, n_tokens, w_gate, w_up, w_down, out);
+}
+
+int et_moe_block(const uint16_t* x, int n_tokens, const uint16_t* w_router,
+                 const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                 const uint16_t* mlp_gate, const uint16_t* mlp_up, const uint16_t* mlp_down,
+                 float* moe_out, float* y, void* ws, const et_plan* plan, int sched,
+                 const et_opts* opts, hipStream_t stream) {
+  LaunchCommon lc;
+  int e = fill_common(lc, ws, plan, sched, opts, stream, ET_WL_BLOCK);
+  if (e) return e;
+  if (n_tokens < 0) return ET_EINVAL;
+  if (n_tokens > plan->max_tokens) return ET_EWORKSPACE;
+  if (n_tokens == 0) return ET_OK;
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !mlp_gate || !mlp_up || !mlp_down ||
+      !moe_out || !y)
+    return ET_EINVAL;
+  return launch_block(lc, x, n_tokens, w_router, w_gate, w_up, w_down, mlp_gate, mlp_up, mlp_down,
+                      moe_out, y);
 }
 
 int et_read_status(const void* ws, const et_plan* plan, hipStream_t stream, et_report* out) {

@@ -46,6 +46,9 @@ int launch_mlp(const LaunchCommon& lc, const uint16_t* x, int B, const uint16_t*
                const uint16_t* wu, const uint16_t* wd, float* y);
 int launch_moe(const LaunchCommon& lc, const float* logits, const uint16_t* x, int T,
                const uint16_t* wg, const uint16_t* wu, const uint16_t* wd, float* out);
+int launch_block(const LaunchCommon& lc, const uint16_t* x, int T, const uint16_t* wr,
+                 const uint16_t* wg, const uint16_t* wu, const uint16_t* wd, const uint16_t* mg,
+                 const uint16_t* mu, const uint16_t* md, float* moe_out, float* y);
 
 // Dense MLP: rows per tile from the batch (stream variants only), unless forced.
 inline int pick_mlp_tile(int batch, int forced) {

@@ -150,7 +150,10 @@ constexpr int kHistEntries = 8192;    // n_route * E must fit (int32, 32 KB of L
 constexpr int kRouteTok = 8;          // tokens per routing chunk (fewer chunks when T is small)
 constexpr int kBcastChunks = 16;      // routing chunks from which their events are broadcast
 
-enum : int { EV_ROUTE = 0, EV_SCAN = 1, EV_GROUP = 2, EV_G1ALL = 3, EV_DOWN = 4, EV_FIXED = 8 };
+// EV_COMB / EV_MG: all combine tiles / all dense MLP gate/up tiles done (the
+// router -> MoE -> dense MLP chain under the barrier schedule)
+enum : int { EV_ROUTE = 0, EV_SCAN = 1, EV_GROUP = 2, EV_G1ALL = 3, EV_DOWN = 4, EV_COMB = 5,
+             EV_MG = 6, EV_FIXED = 8 };
 
 // per-call metadata words (HDR_META + i), written by the scan task
 enum : int { MD_NB = 0, MD_TOTAL1 = 1, MD_TOTAL2 = 2 };
@@ -184,6 +187,29 @@ ET_HD int moe_n_route(int n_experts) {
   return r > 128 ? 128 : (r < 1 ? 1 : r);
 }
 
+// ---------------------------------------------------------------------------
+// Router GEMM -> MoE layer -> dense MLP chain: the MoE layer's events and
+// tasks, then the dense MLP's.  The MLP runs on row blocks of mrows(T)
+// tokens (16 while the MoE uses its 16-row variants, else 64).
+// events (after the MoE layer's n_events_max()):
+//   E_z[mb]      combine tiles covering the tokens of MLP row block mb
+//                (16-token groups of the block x combine column tiles)
+//   E_hm[mb][n]  dense MLP gate/up tiles of 128-column h tile n (8)
+// tasks (after the MoE layer's, whose combine always runs as tiles): the
+//   gate/up tiles (mb, n < Im/16), then the down tiles (mb, n2 < H/16).
+// ---------------------------------------------------------------------------
+struct BlockPlan {
+  MoePlan moe;
+  int mlp_inter;
+  ET_HD int nmb_max() const { return cdiv(moe.t_max, kMinRows); }
+  ET_HD int ev_z() const { return moe.n_events_max(); }
+  ET_HD int ev_hm() const { return ev_z() + nmb_max(); }
+  ET_HD int n_events_max() const { return ev_hm() + nmb_max() * (mlp_inter / kHTile); }
+  ET_HD int max_tasks() const {
+    return moe.max_tasks() + nmb_max() * (mlp_inter / kMinCols + moe.hidden / kMinCols);
+  }
+};
+
 // Byte offsets of the MoE intermediates inside the aux region.
 struct MoeAux {
   size_t topk_ids, topk_w, hist, counts, tok_indptr, blk_indptr, task_indptr, perm, inv, h, y,
@@ -206,6 +232,25 @@ inline MoeAux moe_aux_layout(const MoePlan& p) {
   a.inv = take(TK * 4);
   a.h = take(TK * p.inter * 2);
   a.y = take(TK * p.hidden * 2);   // bf16 down-projection rows
+  a.bytes = o;
+  return a;
+}
+
+// The chain's intermediates after the MoE layer's: router logits, the MoE
+// output in bf16 (the dense MLP's input), the dense MLP's h.
+struct BlockAux {
+  MoeAux moe;
+  size_t logits, zb, h2, bytes;
+};
+
+inline BlockAux block_aux_layout(const BlockPlan& p) {
+  BlockAux a;
+  a.moe = moe_aux_layout(p.moe);
+  size_t o = a.moe.bytes;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes, 256); return r; };
+  a.logits = take((size_t)p.moe.t_max * p.moe.n_experts * 4);
+  a.zb = take((size_t)p.moe.t_max * p.moe.hidden * 2);
+  a.h2 = take((size_t)p.moe.t_max * p.mlp_inter * 2);
   a.bytes = o;
   return a;
 }

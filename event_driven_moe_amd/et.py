@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "et.h")
 SCHED_STATIC, SCHED_DYNAMIC, SCHED_BARRIER, SCHED_PER_OP = 0, 1, 2, 3
 SCHEDS = {"static": 0, "dynamic": 1, "barrier": 2, "per_op": 3}
 OK, EINVAL, EWORKSPACE, EHIP, ETIMEOUT, EUNSUPPORTED, ESTATE = range(7)
-WL_SPLITK, WL_MLP, WL_MOE = 1, 2, 3
+WL_SPLITK, WL_MLP, WL_MOE, WL_BLOCK = 1, 2, 3, 4
 DEBUG_COUNTS, DEBUG_TRACE, SCRATCH_RESET = 1, 2, 4
 
 c_int, c_size_t, c_void_p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
@@ -36,7 +36,7 @@ class Plan(ctypes.Structure):
                 ("max_tasks", c_int), ("bytes", c_size_t), ("off_counters", c_size_t),
                 ("off_slots", c_size_t), ("off_runs", c_size_t), ("off_trace", c_size_t),
                 ("off_aux", c_size_t),
-                ("aux_bytes", c_size_t)]
+                ("aux_bytes", c_size_t), ("mlp_inter", c_int)]
 
 
 class Layout(ctypes.Structure):
@@ -44,7 +44,8 @@ class Layout(ctypes.Structure):
                 ("trace", c_size_t),
                 ("topk_ids", c_size_t), ("topk_w", c_size_t), ("counts", c_size_t),
                 ("tok_indptr", c_size_t), ("perm", c_size_t), ("inv", c_size_t),
-                ("task_indptr", c_size_t), ("h", c_size_t), ("y", c_size_t)]
+                ("task_indptr", c_size_t), ("h", c_size_t), ("y", c_size_t),
+                ("logits", c_size_t), ("z", c_size_t), ("h2", c_size_t)]
 
 
 class Report(ctypes.Structure):
@@ -80,6 +81,9 @@ def lib():
                              P(Plan), c_int, P(Opts), c_void_p]
         L.et_moe_layer.argtypes = [c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_void_p, P(Plan), c_int, P(Opts), c_void_p]
+        L.et_plan_block.argtypes = [c_int] * 6 + [P(Plan)]
+        L.et_moe_block.argtypes = [c_void_p, c_int] + [c_void_p] * 10 + [P(Plan), c_int, P(Opts),
+                                                                       c_void_p]
         L.et_moe_layer_noalloc.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                                            c_void_p, c_void_p, c_void_p, c_void_p, c_int,
                                            P(Opts), c_void_p]
@@ -91,6 +95,7 @@ def lib():
         L.et_num_workers.argtypes = []
         for f in ("et_plan_workspace", "et_workspace_init", "et_workspace_layout",
                   "et_splitk_reduce", "et_mlp", "et_moe_layer", "et_moe_layer_noalloc",
+                  "et_plan_block", "et_moe_block",
                   "et_read_status", "et_num_workers", "et_ceiling_mfma", "et_ceiling_stream"):
             getattr(L, f).restype = c_int
         _lib = L
@@ -144,10 +149,14 @@ def _opts(fetch_batch=4, debug=0, timeout_ms=2000, tile=-1, cooperative=False, q
                 LAUNCH_COOPERATIVE if cooperative else LAUNCH_ORDINARY, queue_shards)
 
 
-def plan_workspace(workload, max_tokens, hidden=0, inter=0, n_experts=0, top_k=0):
+def plan_workspace(workload, max_tokens, hidden=0, inter=0, n_experts=0, top_k=0, mlp_inter=0):
     p = Plan()
-    _check(lib().et_plan_workspace(workload, max_tokens, hidden, inter, n_experts, top_k,
-                                   ctypes.byref(p)), "et_plan_workspace")
+    if workload == WL_BLOCK:
+        _check(lib().et_plan_block(max_tokens, hidden, inter, n_experts, top_k, mlp_inter,
+                                   ctypes.byref(p)), "et_plan_block")
+    else:
+        _check(lib().et_plan_workspace(workload, max_tokens, hidden, inter, n_experts, top_k,
+                                       ctypes.byref(p)), "et_plan_workspace")
     return p
 
 
@@ -156,8 +165,9 @@ class Workspace:
     intermediates, sized by et_plan_workspace and cleared by et_workspace_init."""
 
     def __init__(self, workload, max_tokens, hidden=0, inter=0, n_experts=0, top_k=0,
-                 device="cuda", stream=None):
-        self.plan = plan_workspace(workload, max_tokens, hidden, inter, n_experts, top_k)
+                 device="cuda", stream=None, mlp_inter=0):
+        self.plan = plan_workspace(workload, max_tokens, hidden, inter, n_experts, top_k,
+                                   mlp_inter)
         self.buf = torch.empty(self.plan.bytes, dtype=torch.uint8, device=device)
         self.init(stream)
 
@@ -248,6 +258,44 @@ def moe_layer(logits, x, w_gate, w_up, w_down, out, ws, sched="dynamic", stream=
     o = _opts(**opts)
     _check(lib().et_moe_layer(*args, ws.ptr, ctypes.byref(ws.plan), SCHEDS.get(sched, sched),
                               ctypes.byref(o), _stream(stream)), "et_moe_layer")
+
+
+def moe_block(x, w_router, w_gate, w_up, w_down, mlp_gate, mlp_up, mlp_down, moe_out, y, ws,
+              sched="static", stream=None, **opts):
+    """x bf16 [T,H]; w_router bf16 [E,H]; experts as for moe_layer; dense MLP
+    mlp_gate/mlp_up bf16 [Im,H], mlp_down bf16 [H,Im]; moe_out, y f32 [T,H]."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    I = w_gate.shape[1]
+    Im = mlp_gate.shape[0]
+    if (H, I, E, Im) != (ws.plan.hidden, ws.plan.inter, ws.plan.n_experts, ws.plan.mlp_inter):
+        raise ValueError("weights do not match the workspace plan")
+    args = (_ptr(x, torch.bfloat16, "x", (T, H)), T,
+            _ptr(w_router, torch.bfloat16, "w_router", (E, H)),
+            _ptr(w_gate, torch.bfloat16, "w_gate", (E, I, H)),
+            _ptr(w_up, torch.bfloat16, "w_up", (E, I, H)),
+            _ptr(w_down, torch.bfloat16, "w_down", (E, H, I)),
+            _ptr(mlp_gate, torch.bfloat16, "mlp_gate", (Im, H)),
+            _ptr(mlp_up, torch.bfloat16, "mlp_up", (Im, H)),
+            _ptr(mlp_down, torch.bfloat16, "mlp_down", (H, Im)),
+            _ptr(moe_out, torch.float32, "moe_out", (T, H)),
+            _ptr(y, torch.float32, "y", (T, H)))
+    o = _opts(**opts)
+    _check(lib().et_moe_block(*args, ws.ptr, ctypes.byref(ws.plan), SCHEDS.get(sched, sched),
+                              ctypes.byref(o), _stream(stream)), "et_moe_block")
+
+
+def block_aux(ws, T):
+    """The chain's intermediates of the last call: router logits (float
+    [T, E]), the MoE output in bf16 (the dense MLP's input, [T, H]) and the
+    dense MLP's h (bf16 [T, Im]), plus the MoE routing views of moe_aux."""
+    lay = ws.layout(T)
+    E, H, Im = ws.plan.n_experts, ws.plan.hidden, ws.plan.mlp_inter
+    aux = moe_aux(ws, T)
+    aux["logits"] = ws.view(lay.logits, torch.float32, T * E).view(T, E)
+    aux["z"] = ws.view(lay.z, torch.bfloat16, T * H).view(T, H)
+    aux["h2"] = ws.view(lay.h2, torch.bfloat16, T * Im).view(T, Im)
+    return aux
 
 
 def moe_layer_noalloc(logits, x, w_gate, w_up, w_down, out, sched="dynamic", stream=None,

@@ -69,7 +69,7 @@ enum {
 };
 
 /* Workloads (a workspace is planned for one of them). */
-enum { ET_WL_SPLITK = 1, ET_WL_MLP = 2, ET_WL_MOE = 3 };
+enum { ET_WL_SPLITK = 1, ET_WL_MLP = 2, ET_WL_MOE = 3, ET_WL_BLOCK = 4 };
 
 /* Debug flags. */
 enum {
@@ -121,6 +121,7 @@ typedef struct et_plan {
   size_t off_trace;    /* int32 [max_tasks][4] task trace + [1024][2] workgroup times (ET_DEBUG_TRACE) */
   size_t off_aux;      /* workload intermediates (see et_layout) */
   size_t aux_bytes;
+  int mlp_inter;       /* ET_WL_BLOCK: intermediate size of the dense MLP (else 0) */
 } et_plan;
 
 /* Where to find things inside a workspace after a call (for checks and
@@ -140,6 +141,9 @@ typedef struct et_layout {
   size_t task_indptr;       /* MoE: int32 [E+1] gate/up tasks per expert (CSR) */
   size_t h;                 /* MLP: bf16 [B, I]; MoE: bf16 [T*k, I] (grouped rows) */
   size_t y;                 /* MoE: bf16 [T*k, H] down-projection rows (grouped rows) */
+  size_t logits;            /* chain: float [T, E] router logits */
+  size_t z;                 /* chain: bf16 [T, H] MoE output rounded to bf16 (the MLP's input) */
+  size_t h2;                /* chain: bf16 [T, Im] dense MLP h */
 } et_layout;
 
 /* Device-side state of a workspace, read back by et_read_status(). */
@@ -216,6 +220,35 @@ int et_mlp(const uint16_t* x, int n_tokens, const uint16_t* w_gate, const uint16
 int et_moe_layer(const float* logits, const uint16_t* x, int n_tokens,
                  const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                  float* out, void* ws, const et_plan* plan, int sched,
+                 const et_opts* opts, hipStream_t stream);
+
+/* Plans a workspace for the router GEMM -> MoE layer -> dense MLP chain
+ * (et_moe_block): the MoE layer's dimensions as for et_plan_workspace(ET_WL_MOE, ...)
+ * plus the dense MLP's intermediate size mlp_inter (a multiple of 128).
+ * Returns ET_OK, ET_EINVAL or ET_EUNSUPPORTED. */
+int et_plan_block(int max_tokens, int hidden, int inter, int n_experts, int top_k,
+                  int mlp_inter, et_plan* plan);
+
+/* Router GEMM -> MoE layer -> dense MLP in ONE persistent launch (Event Tensor
+ * notes, section "端到端低 batch serving": the MoE GroupGEMM pipelined with the
+ * dense MLP GEMM across stages, the next stage's weights fetched before its
+ * activations arrive).
+ *   x         bf16 [T, H], T = n_tokens (runtime, <= plan.max_tokens)
+ *   w_router  bf16 [E, H]  = W_router [H, E] transposed (row e holds column e)
+ *   w_gate, w_up bf16 [E, I, H], w_down bf16 [E, H, I]: the experts, as for et_moe_layer
+ *   mlp_gate, mlp_up bf16 [Im, H], mlp_down bf16 [H, Im]: the dense MLP, as for et_mlp
+ *   moe_out   float [T, H] out: z = the MoE layer on x with logits = x W_router
+ *   y         float [T, H] out: y = (SiLU(z' Wg) * (z' Wu)) Wd, z' = z rounded to bf16
+ * The routing task of each token chunk computes the chunk's logits (fp32
+ * accumulation; kept in the workspace, et_layout.logits) before ranking them; the
+ * combine writes z and its bf16 copy; a dense MLP gate/up tile of a row block waits
+ * on the event of that block's combine tiles (E_z, a cross-operator event) after
+ * starting its weight stream, and its down tiles wait per 128-column h tile.  All
+ * four schedules; the MoE combine always runs as tiles.  Errors as for et_moe_layer. */
+int et_moe_block(const uint16_t* x, int n_tokens, const uint16_t* w_router,
+                 const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                 const uint16_t* mlp_gate, const uint16_t* mlp_up, const uint16_t* mlp_down,
+                 float* moe_out, float* y, void* ws, const et_plan* plan, int sched,
                  const et_opts* opts, hipStream_t stream);
 
 /* Allocation-free variant of et_moe_layer, for callers that cannot allocate device
