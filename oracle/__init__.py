@@ -22,4 +22,4 @@ Parity status of each function is stated in its module header; functions that
 have no pin are marked "parity unpinned" there.
 """
 
-from . import splitk, mlp, moe, events, block  # noqa: F401
+from . import splitk, mlp, moe, events, block, decode  # noqa: F401
