@@ -89,6 +89,7 @@ def test_decode_step_appends_at_pos():
     q, k, v = rng.standard_normal((B, Hq, D)), rng.standard_normal((B, Hk, D)), rng.standard_normal((B, Hk, D))
     kc, vc = rng.standard_normal((B, S, Hk, D)), rng.standard_normal((B, S, Hk, D))
     pos = np.array([0, 3])
+    kc0, vc0 = kc.copy(), vc.copy()
     qr, kr, out = decode.decode_step(q, k, v, np.ones(D), np.ones(D), pos, 1e4, 1e-6, kc, vc)
     # sequence 0 attends to its new token only
     for j in range(Hq):
@@ -97,4 +98,4 @@ def test_decode_step_appends_at_pos():
     K = kc[1, :4].copy(); K[3] = kr[1]
     V = vc[1, :4].copy(); V[3] = v[1]
     assert np.allclose(out[1], decode.attention(qr[1], K, V, 4))
-    assert np.array_equal(kc[1, 3], kc[1, 3])   # inputs untouched
+    assert np.array_equal(kc, kc0) and np.array_equal(vc, vc0)   # inputs untouched
