@@ -13,7 +13,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libet.so")
 OBJDIR = os.path.join(ROOT, "_build")
-SOURCES = ["et_moe.hip", "et_block.hip", "et_api.hip", "et_splitk.hip", "et_mlp.hip", "et_ceiling.hip"]
+SOURCES = ["et_moe.hip", "et_block.hip", "et_api.hip", "et_splitk.hip", "et_mlp.hip", "et_decode.hip",
+           "et_ceiling.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

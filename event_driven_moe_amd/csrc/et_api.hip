@@ -260,7 +260,9 @@ int et_workspace_layout(const et_plan* plan, int n_tokens, et_layout* out) {
   out->n_events = plan->n_events;
   out->runs = plan->off_runs;
   out->trace = plan->off_trace;
-  if (plan->workload == ET_WL_MLP) {
+  if (plan->workload == ET_WL_DECODE) {
+    out->q_rot = plan->off_aux;
+  } else if (plan->workload == ET_WL_MLP) {
     out->h = plan->off_aux;
   } else if (plan->workload == ET_WL_MOE || plan->workload == ET_WL_BLOCK) {
     MoePlan p{plan->max_tokens, plan->hidden, plan->inter, plan->n_experts, plan->top_k,
@@ -323,6 +325,45 @@ int et_moe_layer(const float* logits, const uint16_t* x, int n_tokens, const uin
   if (n_tokens == 0) return ET_OK;
   if (!logits || !x || !w_gate || !w_up || !w_down || !out) return ET_EINVAL;
   return launch_moe(lc, logits, x, n_tokens, w_gate, w_up, w_down, out);
+}
+
+int et_plan_decode(int max_batch, int n_heads, int n_kv_heads, int head_dim, et_plan* plan) {
+  if (!plan) return ET_EINVAL;
+  std::memset(plan, 0, sizeof(*plan));
+  if (max_batch <= 0 || n_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0) return ET_EINVAL;
+  if (n_heads % n_kv_heads) return ET_EINVAL;
+  if (head_dim != 128 || n_heads / n_kv_heads > 16) return ET_EUNSUPPORTED;
+  if ((size_t)max_batch * n_heads * head_dim * 4 >= (1ull << 31) ||
+      (size_t)max_batch * n_kv_heads * 3 >= (1ull << 30))
+    return ET_EUNSUPPORTED;
+  plan->workload = ET_WL_DECODE;
+  plan->max_tokens = max_batch;
+  plan->hidden = head_dim;
+  plan->n_heads = n_heads;
+  plan->n_kv_heads = n_kv_heads;
+  plan->n_events = 8 + max_batch * n_kv_heads;
+  plan->max_tasks = 3 * max_batch * n_kv_heads;
+  finish_plan(plan, (size_t)max_batch * n_heads * head_dim * 4);
+  return ET_OK;
+}
+
+int et_decode_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const uint16_t* q_norm_w, const uint16_t* k_norm_w, const int32_t* pos,
+                        int n_seqs, float rope_theta, float eps, uint16_t* k_cache,
+                        uint16_t* v_cache, int max_seq, float* out, void* ws,
+                        const et_plan* plan, int sched, const et_opts* opts, hipStream_t stream) {
+  LaunchCommon lc;
+  int e = fill_common(lc, ws, plan, sched, opts, stream, ET_WL_DECODE);
+  if (e) return e;
+  if (n_seqs < 0 || max_seq <= 0 || !(rope_theta > 1.0f) || !(eps >= 0.0f)) return ET_EINVAL;
+  if (n_seqs > plan->max_tokens) return ET_EWORKSPACE;
+  if (n_seqs == 0) return ET_OK;
+  if (!q || !k || !v || !q_norm_w || !k_norm_w || !pos || !k_cache || !v_cache || !out)
+    return ET_EINVAL;
+  if ((size_t)n_seqs * max_seq * plan->n_kv_heads * plan->hidden * 2 >= (1ull << 32))
+    return ET_EUNSUPPORTED;
+  return launch_decode(lc, q, k, v, q_norm_w, k_norm_w, pos, n_seqs, rope_theta, eps, k_cache,
+                       v_cache, max_seq, out);
 }
 
 int et_moe_block(const uint16_t* x, int n_tokens, const uint16_t* w_router,
@@ -424,6 +465,7 @@ const char* et_status_str(int s) {
     case ET_ETIMEOUT: return "device wait exceeded the watchdog";
     case ET_EUNSUPPORTED: return "unsupported dimensions";
     case ET_ESTATE: return "event over-notified or ready queue overflow";
+    case ET_ERANGE: return "device input index out of range";
     default: return "unknown status";
   }
 }

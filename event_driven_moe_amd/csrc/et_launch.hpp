@@ -46,6 +46,9 @@ int launch_mlp(const LaunchCommon& lc, const uint16_t* x, int B, const uint16_t*
                const uint16_t* wu, const uint16_t* wd, float* y);
 int launch_moe(const LaunchCommon& lc, const float* logits, const uint16_t* x, int T,
                const uint16_t* wg, const uint16_t* wu, const uint16_t* wd, float* out);
+int launch_decode(const LaunchCommon& lc, const uint16_t* q, const uint16_t* k,
+                  const uint16_t* v, const uint16_t* wq, const uint16_t* wk, const int* pos,
+                  int B, float theta, float eps, uint16_t* kc, uint16_t* vc, int S, float* out);
 int launch_block(const LaunchCommon& lc, const uint16_t* x, int T, const uint16_t* wr,
                  const uint16_t* wg, const uint16_t* wu, const uint16_t* wd, const uint16_t* mg,
                  const uint16_t* mu, const uint16_t* md, float* moe_out, float* y);

@@ -18,8 +18,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "et.h")
 
 SCHED_STATIC, SCHED_DYNAMIC, SCHED_BARRIER, SCHED_PER_OP = 0, 1, 2, 3
 SCHEDS = {"static": 0, "dynamic": 1, "barrier": 2, "per_op": 3}
-OK, EINVAL, EWORKSPACE, EHIP, ETIMEOUT, EUNSUPPORTED, ESTATE = range(7)
-WL_SPLITK, WL_MLP, WL_MOE, WL_BLOCK = 1, 2, 3, 4
+OK, EINVAL, EWORKSPACE, EHIP, ETIMEOUT, EUNSUPPORTED, ESTATE, ERANGE = range(8)
+WL_SPLITK, WL_MLP, WL_MOE, WL_BLOCK, WL_DECODE = 1, 2, 3, 4, 5
 DEBUG_COUNTS, DEBUG_TRACE, SCRATCH_RESET = 1, 2, 4
 
 c_int, c_size_t, c_void_p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
@@ -36,7 +36,8 @@ class Plan(ctypes.Structure):
                 ("max_tasks", c_int), ("bytes", c_size_t), ("off_counters", c_size_t),
                 ("off_slots", c_size_t), ("off_runs", c_size_t), ("off_trace", c_size_t),
                 ("off_aux", c_size_t),
-                ("aux_bytes", c_size_t), ("mlp_inter", c_int)]
+                ("aux_bytes", c_size_t), ("mlp_inter", c_int), ("n_heads", c_int),
+                ("n_kv_heads", c_int)]
 
 
 class Layout(ctypes.Structure):
@@ -45,7 +46,7 @@ class Layout(ctypes.Structure):
                 ("topk_ids", c_size_t), ("topk_w", c_size_t), ("counts", c_size_t),
                 ("tok_indptr", c_size_t), ("perm", c_size_t), ("inv", c_size_t),
                 ("task_indptr", c_size_t), ("h", c_size_t), ("y", c_size_t),
-                ("logits", c_size_t), ("z", c_size_t), ("h2", c_size_t)]
+                ("logits", c_size_t), ("z", c_size_t), ("h2", c_size_t), ("q_rot", c_size_t)]
 
 
 class Report(ctypes.Structure):
@@ -82,6 +83,10 @@ def lib():
         L.et_moe_layer.argtypes = [c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                    c_void_p, c_void_p, P(Plan), c_int, P(Opts), c_void_p]
         L.et_plan_block.argtypes = [c_int] * 6 + [P(Plan)]
+        L.et_plan_decode.argtypes = [c_int] * 4 + [P(Plan)]
+        L.et_decode_attention.argtypes = ([c_void_p] * 6 + [c_int, ctypes.c_float, ctypes.c_float] +
+                                          [c_void_p, c_void_p, c_int, c_void_p, c_void_p, P(Plan),
+                                           c_int, P(Opts), c_void_p])
         L.et_moe_block.argtypes = [c_void_p, c_int] + [c_void_p] * 10 + [P(Plan), c_int, P(Opts),
                                                                        c_void_p]
         L.et_moe_layer_noalloc.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
@@ -95,7 +100,7 @@ def lib():
         L.et_num_workers.argtypes = []
         for f in ("et_plan_workspace", "et_workspace_init", "et_workspace_layout",
                   "et_splitk_reduce", "et_mlp", "et_moe_layer", "et_moe_layer_noalloc",
-                  "et_plan_block", "et_moe_block",
+                  "et_plan_block", "et_moe_block", "et_plan_decode", "et_decode_attention",
                   "et_read_status", "et_num_workers", "et_ceiling_mfma", "et_ceiling_stream"):
             getattr(L, f).restype = c_int
         _lib = L
@@ -149,9 +154,13 @@ def _opts(fetch_batch=4, debug=0, timeout_ms=2000, tile=-1, cooperative=False, q
                 LAUNCH_COOPERATIVE if cooperative else LAUNCH_ORDINARY, queue_shards)
 
 
-def plan_workspace(workload, max_tokens, hidden=0, inter=0, n_experts=0, top_k=0, mlp_inter=0):
+def plan_workspace(workload, max_tokens, hidden=0, inter=0, n_experts=0, top_k=0, mlp_inter=0,
+                   n_heads=0, n_kv_heads=0, head_dim=0):
     p = Plan()
-    if workload == WL_BLOCK:
+    if workload == WL_DECODE:    # max_tokens: sequences
+        _check(lib().et_plan_decode(max_tokens, n_heads, n_kv_heads, head_dim, ctypes.byref(p)),
+               "et_plan_decode")
+    elif workload == WL_BLOCK:
         _check(lib().et_plan_block(max_tokens, hidden, inter, n_experts, top_k, mlp_inter,
                                    ctypes.byref(p)), "et_plan_block")
     else:
@@ -165,9 +174,9 @@ class Workspace:
     intermediates, sized by et_plan_workspace and cleared by et_workspace_init."""
 
     def __init__(self, workload, max_tokens, hidden=0, inter=0, n_experts=0, top_k=0,
-                 device="cuda", stream=None, mlp_inter=0):
+                 device="cuda", stream=None, mlp_inter=0, n_heads=0, n_kv_heads=0, head_dim=0):
         self.plan = plan_workspace(workload, max_tokens, hidden, inter, n_experts, top_k,
-                                   mlp_inter)
+                                   mlp_inter, n_heads, n_kv_heads, head_dim)
         self.buf = torch.empty(self.plan.bytes, dtype=torch.uint8, device=device)
         self.init(stream)
 
@@ -283,6 +292,34 @@ def moe_block(x, w_router, w_gate, w_up, w_down, mlp_gate, mlp_up, mlp_down, moe
     o = _opts(**opts)
     _check(lib().et_moe_block(*args, ws.ptr, ctypes.byref(ws.plan), SCHEDS.get(sched, sched),
                               ctypes.byref(o), _stream(stream)), "et_moe_block")
+
+
+def decode_attention(q, k, v, q_norm_w, k_norm_w, pos, k_cache, v_cache, out, ws,
+                     sched="static", rope_theta=1e6, eps=1e-6, stream=None, **opts):
+    """q bf16 [B,Hq,D]; k, v bf16 [B,Hk,D]; norm weights bf16 [D]; pos int32 [B];
+    caches bf16 [B,S,Hk,D] (updated in place); out f32 [B,Hq,D]."""
+    B, Hq, D = q.shape
+    Hk = k.shape[1]
+    S = k_cache.shape[1]
+    if (Hq, Hk, D) != (ws.plan.n_heads, ws.plan.n_kv_heads, ws.plan.hidden):
+        raise ValueError("heads do not match the workspace plan")
+    args = (_ptr(q, torch.bfloat16, "q", (B, Hq, D)), _ptr(k, torch.bfloat16, "k", (B, Hk, D)),
+            _ptr(v, torch.bfloat16, "v", (B, Hk, D)), _ptr(q_norm_w, torch.bfloat16, "q_norm_w", (D,)),
+            _ptr(k_norm_w, torch.bfloat16, "k_norm_w", (D,)), _ptr(pos, torch.int32, "pos", (B,)),
+            B, float(rope_theta), float(eps),
+            _ptr(k_cache, torch.bfloat16, "k_cache", (B, S, Hk, D)),
+            _ptr(v_cache, torch.bfloat16, "v_cache", (B, S, Hk, D)), S,
+            _ptr(out, torch.float32, "out", (B, Hq, D)))
+    o = _opts(**opts)
+    _check(lib().et_decode_attention(*args, ws.ptr, ctypes.byref(ws.plan), SCHEDS.get(sched, sched),
+                                     ctypes.byref(o), _stream(stream)), "et_decode_attention")
+
+
+def decode_q_rot(ws, B):
+    """The normalised, rotated queries of the last decode call (float [B, Hq, D])."""
+    lay = ws.layout(B)
+    Hq, D = ws.plan.n_heads, ws.plan.hidden
+    return ws.view(lay.q_rot, torch.float32, B * Hq * D).view(B, Hq, D)
 
 
 def block_aux(ws, T):

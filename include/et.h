@@ -65,11 +65,13 @@ enum {
   ET_EHIP = 3,          /* a HIP runtime call failed */
   ET_ETIMEOUT = 4,      /* device: a wait or a queue slot exceeded the watchdog */
   ET_EUNSUPPORTED = 5,  /* dimensions the kernels do not tile (see each entry point) */
-  ET_ESTATE = 6         /* device: an event was over-notified or the ready queue overflowed */
+  ET_ESTATE = 6,        /* device: an event was over-notified or the ready queue overflowed */
+  ET_ERANGE = 7         /* device: an index read from a device input is out of range (a decode
+                           position outside the cache) */
 };
 
 /* Workloads (a workspace is planned for one of them). */
-enum { ET_WL_SPLITK = 1, ET_WL_MLP = 2, ET_WL_MOE = 3, ET_WL_BLOCK = 4 };
+enum { ET_WL_SPLITK = 1, ET_WL_MLP = 2, ET_WL_MOE = 3, ET_WL_BLOCK = 4, ET_WL_DECODE = 5 };
 
 /* Debug flags. */
 enum {
@@ -122,6 +124,8 @@ typedef struct et_plan {
   size_t off_aux;      /* workload intermediates (see et_layout) */
   size_t aux_bytes;
   int mlp_inter;       /* ET_WL_BLOCK: intermediate size of the dense MLP (else 0) */
+  int n_heads;         /* ET_WL_DECODE: query heads Hq (else 0) */
+  int n_kv_heads;      /* ET_WL_DECODE: key/value heads Hk (else 0) */
 } et_plan;
 
 /* Where to find things inside a workspace after a call (for checks and
@@ -144,6 +148,7 @@ typedef struct et_layout {
   size_t logits;            /* chain: float [T, E] router logits */
   size_t z;                 /* chain: bf16 [T, H] MoE output rounded to bf16 (the MLP's input) */
   size_t h2;                /* chain: bf16 [T, Im] dense MLP h */
+  size_t q_rot;             /* decode: float [B, Hq, D] normalised and rotated queries */
 } et_layout;
 
 /* Device-side state of a workspace, read back by et_read_status(). */
@@ -250,6 +255,36 @@ int et_moe_block(const uint16_t* x, int n_tokens, const uint16_t* w_router,
                  const uint16_t* mlp_gate, const uint16_t* mlp_up, const uint16_t* mlp_down,
                  float* moe_out, float* y, void* ws, const et_plan* plan, int sched,
                  const et_opts* opts, hipStream_t stream);
+
+/* Plans a workspace for et_decode_attention: up to max_batch sequences, n_heads
+ * query heads sharing n_kv_heads key/value heads (n_heads a multiple of n_kv_heads,
+ * at most 16 query heads per key/value head), head_dim 128.
+ * Returns ET_OK, ET_EINVAL or ET_EUNSUPPORTED. */
+int et_plan_decode(int max_batch, int n_heads, int n_kv_heads, int head_dim, et_plan* plan);
+
+/* One decode step's attention front in ONE persistent launch (Event Tensor notes,
+ * section "端到端低 batch serving": the query branch's Norm + RoPE runs in parallel
+ * with the key branch's Norm + RoPE + cache append).
+ *   q        bf16 [B, Hq, D], k, v bf16 [B, Hk, D]: the new token of each sequence,
+ *            B = n_seqs (runtime, <= plan.max_tokens), D = 128
+ *   q_norm_w, k_norm_w bf16 [D]: RMSNorm weights, applied per head with `eps`
+ *   pos      int32 [B] (device): position of each sequence's new token; the caches
+ *            hold positions 0 .. pos[b]-1 and pos[b] < max_seq (else ET_ERANGE on
+ *            the device)
+ *   k_cache, v_cache bf16 [B, max_seq, Hk, D], updated in place: position pos[b]
+ *            receives the rotated key (rounded to bf16) and the value row
+ *   out      float [B, Hq, D] out: softmax(q' K^T / sqrt(D)) V over positions
+ *            0 .. pos[b], query head j reading key/value head j / (Hq / Hk)
+ * q' and k' are RMSNorm(x) * w rotated pairwise: elements (i, i + D/2) by the angle
+ * pos * rope_theta^(-2i/D).  Query-branch task (b, h) and key-branch task (b, h)
+ * both notify E_qk[b, h] (wait count 2), on which the attention task (b, h) waits;
+ * the static and dynamic schedules run the two branches side by side.  Errors as for
+ * et_moe_layer. */
+int et_decode_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const uint16_t* q_norm_w, const uint16_t* k_norm_w, const int32_t* pos,
+                        int n_seqs, float rope_theta, float eps, uint16_t* k_cache,
+                        uint16_t* v_cache, int max_seq, float* out, void* ws,
+                        const et_plan* plan, int sched, const et_opts* opts, hipStream_t stream);
 
 /* Allocation-free variant of et_moe_layer, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
