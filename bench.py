@@ -238,6 +238,68 @@ def ceilings():
     print(json.dumps(res))
 
 
+def bench_chain(args):
+    """The router GEMM -> MoE -> dense MLP chain (et_moe_block) or the decode
+    attention front (et_decode_attention): time per call under every
+    schedule, with the algorithmic bytes of the call against HBM."""
+    import torch
+    from event_driven_moe_amd import et, synth
+    dev = "cuda"
+    T = args.tokens
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    if args.workload.startswith("block_"):
+        cfg = synth.MOE_PRESETS[args.workload[len("block_"):]]
+        H, I, E, k, Im = cfg["hidden"], cfg["inter"], cfg["n_experts"], cfg["top_k"], 5632
+        _, x = synth.moe_activations(cfg, T, device=dev)
+        wr = synth.k_major(synth.normal_bf16((H, E), 0.02, 700 + E, dev))
+        wg, wu, wd = synth.moe_weights_k_major(cfg, device=dev)
+        _, mg, mu, md = synth.mlp_inputs(1, H, Im, device=dev)
+        mg, mu, md = synth.k_major(mg), synth.k_major(mu), synth.k_major(md)
+        ws = et.Workspace(et.WL_BLOCK, T, H, I, E, k, device=dev, mlp_inter=Im)
+        z = torch.empty((T, H), device=dev)
+        y = torch.empty((T, H), device=dev)
+        call = lambda s: et.moe_block(x, wr, wg, wu, wd, mg, mu, md, z, y, ws, s)
+        call("static")
+        torch.cuda.synchronize()
+        n_active = int((et.moe_aux(ws, T)["counts"] > 0).sum().item())
+        nbytes = (n_active * 3 * H * I * 2 + 3 * H * Im * 2 + E * H * 2 + T * H * 2 + 2 * T * H * 4)
+        flops = 2 * T * H * E + 2 * 3 * H * I * T * k + 2 * 3 * H * Im * T
+        desc = ("router GEMM -> MoE layer (%s shapes: hidden %d, %d experts, top-%d, intermediate "
+                "%d; %d active) -> dense MLP (intermediate %d), %d tokens, one launch"
+                % (cfg["name"], H, E, k, I, n_active, Im, T))
+    else:
+        Hq, Hk, D, S = 64, 8, 128, 1024
+        B = T
+        q = synth.normal_bf16((B, Hq, D), 1.0, 800, dev)
+        kk = synth.normal_bf16((B, Hk, D), 1.0, 801, dev)
+        v = synth.normal_bf16((B, Hk, D), 1.0, 802, dev)
+        wq = torch.ones(D, dtype=torch.bfloat16, device=dev)
+        kc = synth.normal_bf16((B, S, Hk, D), 1.0, 805, dev)
+        vc = synth.normal_bf16((B, S, Hk, D), 1.0, 806, dev)
+        g = torch.Generator(device="cpu").manual_seed(807)
+        pos = torch.randint(512, 612, (B,), generator=g).to(torch.int32).to(dev)
+        out = torch.empty((B, Hq, D), device=dev)
+        ws = et.Workspace(et.WL_DECODE, B, device=dev, n_heads=Hq, n_kv_heads=Hk, head_dim=D)
+        call = lambda s: et.decode_attention(q, kk, v, wq, wq, pos, kc, vc, out, ws, s)
+        ctx = int((pos.long() + 1).sum().item())
+        nbytes = ctx * Hk * D * 2 * 2 + B * (Hq + 2 * Hk) * D * 2 + B * Hq * D * 4
+        flops = 4 * ctx * Hq * D
+        desc = ("decode attention front (Qwen3-32B attention: 64 query heads, 8 key/value heads, "
+                "head dim 128), %d sequences at positions 512..611 of a 1024-entry cache" % B)
+    modes = {}
+    for s in ("static", "dynamic", "barrier", "per_op"):
+        log("bench: %s %s" % (args.workload, s))
+        p, _ = time_calls(lambda: call(s), args.steps, args.warmup)
+        modes[s] = round(1e3 * sum(p) / len(p), 2)
+    if ws.status()["status"] != 0:
+        raise SystemExit("device fault: %s" % ws.status())
+    best = min(modes.values())
+    print(json.dumps({"workload": desc, "tokens": T, "us_per_call_by_schedule": modes,
+                      "algorithmic_bytes": nbytes, "flops": flops,
+                      "hbm_frac_best": round(nbytes / (best * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                      "mfma_frac_best": round(flops / (best * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS, 4)}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,6 +331,9 @@ def main():
         return
     if args.ceilings:
         ceilings()
+        return
+    if args.workload.startswith("block_") or args.workload == "decode":
+        bench_chain(args)
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "

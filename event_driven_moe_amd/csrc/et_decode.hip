@@ -172,33 +172,43 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
     float o[kMaxGroup][2];
 #pragma unroll
     for (int g = 0; g < kMaxGroup; ++g) o[g][0] = o[g][1] = 0.f;
+    // The newest position (n - 1) was written in this launch and is read
+    // with coherent loads; the others are inputs.  Loads are issued in
+    // batches before their values are used (a load per use put a full
+    // memory latency on every position).
+    const int qlast = n - 1;
+    const Rsrc rv = make_rsrc(a.vc + base, (uint32_t)((size_t)n * rstride * 2));
     for (int c0 = 0; c0 < n; c0 += kAttnChunk) {
-      // scores of position c0 + tid for every head of the group; the newest
-      // position was written in this launch and is read coherently
+      // scores of position c0 + tid for every head of the group
       const int pp = c0 + tid;
+      const uint32_t off = pp < n ? (uint32_t)(pp * rstride * 2) : kOOB;
+      i32x4 kr[kHeadDim / 8];
+      if (pp == qlast) {
+#pragma unroll
+        for (int j = 0; j < kHeadDim / 8; ++j) kr[j] = ld16c(rk, off + 16u * j);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kHeadDim / 8; ++j) kr[j] = ld16(rk, off + 16u * j);
+      }
       float s[kMaxGroup];
 #pragma unroll
       for (int g = 0; g < kMaxGroup; ++g) s[g] = 0.f;
-      if (pp < n) {
-        const uint32_t off = (uint32_t)(pp * rstride * 2);
-#pragma unroll 4
-        for (int j = 0; j < kHeadDim / 8; ++j) {
-          const i32x4 kv = pp == n - 1 ? ld16c(rk, off + 16u * j) : ld16(rk, off + 16u * j);
-          float kf[8];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            kf[2 * t] = __builtin_bit_cast(float, (uint32_t)kv[t] << 16);
-            kf[2 * t + 1] = __builtin_bit_cast(float, (uint32_t)kv[t] & 0xffff0000u);
-          }
+      for (int j = 0; j < kHeadDim / 8; ++j) {
+        float kf[8];
 #pragma unroll
-          for (int g = 0; g < kMaxGroup; ++g)
-            if (g < G) {
-              const float4 qa = *reinterpret_cast<const float4*>(&qs[g][8 * j]);
-              const float4 qb = *reinterpret_cast<const float4*>(&qs[g][8 * j + 4]);
-              s[g] += qa.x * kf[0] + qa.y * kf[1] + qa.z * kf[2] + qa.w * kf[3] +
-                      qb.x * kf[4] + qb.y * kf[5] + qb.z * kf[6] + qb.w * kf[7];
-            }
+        for (int t = 0; t < 4; ++t) {
+          kf[2 * t] = __builtin_bit_cast(float, (uint32_t)kr[j][t] << 16);
+          kf[2 * t + 1] = __builtin_bit_cast(float, (uint32_t)kr[j][t] & 0xffff0000u);
         }
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g)
+          if (g < G) {
+            const float4 qa = *reinterpret_cast<const float4*>(&qs[g][8 * j]);
+            const float4 qb = *reinterpret_cast<const float4*>(&qs[g][8 * j + 4]);
+            s[g] += qa.x * kf[0] + qa.y * kf[1] + qa.z * kf[2] + qa.w * kf[3] +
+                    qb.x * kf[4] + qb.y * kf[5] + qb.z * kf[6] + qb.w * kf[7];
+          }
       }
       for (int g = 0; g < G; ++g) sc[g][tid] = pp < n ? s[g] * scale : -__builtin_inff();
       __syncthreads();
@@ -224,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
       }
       __syncthreads();
       // value rows: wave w takes positions c0 + w, c0 + w + 4, ...; lane dp
-      // columns 2 dp, 2 dp + 1 of every head
+      // columns 2 dp, 2 dp + 1 of every head; 16 rows requested per batch
 #pragma unroll
       for (int g = 0; g < kMaxGroup; ++g)
         if (g < G) {
@@ -232,9 +242,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
           o[g][1] *= alpha[g];
         }
       const int cend = min(n, c0 + kAttnChunk);
-      for (int q = c0 + wave; q < cend; q += 4) {
-        const uint32_t* vp = reinterpret_cast<const uint32_t*>(a.vc + base + q * rstride) + dp;
-        const uint32_t two = q == n - 1 ? ld_coh(vp) : *vp;
+      const int vend = min(cend, qlast);       // input rows (plain loads)
+      auto add_row = [&](int q, uint32_t two) ET_INLINE {
         const float v0 = __builtin_bit_cast(float, two << 16);
         const float v1 = __builtin_bit_cast(float, two & 0xffff0000u);
 #pragma unroll
@@ -244,7 +253,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
             o[g][0] += e * v0;
             o[g][1] += e * v1;
           }
+      };
+      for (int q0 = c0 + wave; q0 < vend; q0 += 4 * 16) {
+        uint32_t vv[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int q = q0 + 4 * t;
+          vv[t] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+              rv, q < vend ? (int)((q * rstride + 2 * dp) * 2) : (int)kOOB, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+          if (q0 + 4 * t < vend) add_row(q0 + 4 * t, vv[t]);
       }
+      if (qlast >= c0 && qlast < cend && ((qlast - c0) & 3) == wave)
+        add_row(qlast, (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                           rv, (int)((qlast * rstride + 2 * dp) * 2), 0, 16));
       __syncthreads();
     }
     // the four waves' partial sums, then the softmax denominator
