@@ -27,7 +27,7 @@ RunArgs LaunchCommon::run_args() const {
   a.sched = sched;
   a.fetch = fetch;
   a.phase = -1;
-  a.timeout = (long long)timeout_ms * 100000ll;
+  a.timeout = (debug & ET_DEBUG_WATCHDOG_TICK) ? 1 : (long long)timeout_ms * 100000ll;
   a.n_init = 0;
   a.total_hint = kUnknownTotal;
   a.extent = 0;
@@ -334,16 +334,21 @@ int et_plan_decode(int max_batch, int n_heads, int n_kv_heads, int head_dim, et_
   if (n_heads % n_kv_heads) return ET_EINVAL;
   if (head_dim != 128 || n_heads / n_kv_heads > 16) return ET_EUNSUPPORTED;
   if ((size_t)max_batch * n_heads * head_dim * 4 >= (1ull << 31) ||
-      (size_t)max_batch * n_kv_heads * 3 >= (1ull << 30))
+      (size_t)max_batch * n_kv_heads * 11 >= (1ull << 30))
     return ET_EUNSUPPORTED;
   plan->workload = ET_WL_DECODE;
   plan->max_tokens = max_batch;
   plan->hidden = head_dim;
   plan->n_heads = n_heads;
   plan->n_kv_heads = n_kv_heads;
-  plan->n_events = 8 + max_batch * n_kv_heads;
-  plan->max_tasks = 3 * max_batch * n_kv_heads;
-  finish_plan(plan, (size_t)max_batch * n_heads * head_dim * 4);
+  // events: E_qk and E_att per (sequence, key/value head); tasks: two
+  // branches, up to 8 attention splits and a merge per (sequence, head);
+  // workspace: rotated queries, then the splits' partial outputs (8 per
+  // query head) and their running maxima and sums
+  plan->n_events = 8 + 2 * max_batch * n_kv_heads;
+  plan->max_tasks = 11 * max_batch * n_kv_heads;
+  const size_t qr = (size_t)max_batch * n_heads * head_dim * 4;
+  finish_plan(plan, qr + 8 * qr + (size_t)max_batch * n_heads * 8 * 2 * 4);
   return ET_OK;
 }
 

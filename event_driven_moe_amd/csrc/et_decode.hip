@@ -9,10 +9,17 @@
 //   key branch    (b, h): RMSNorm + RoPE of key head h -> appended to the key
 //                 cache at position pos[b] (bf16); the value row appended to
 //                 the value cache;
-//   attention     (b, h): waits on E_qk[i] (wait count 2: one notify from
-//                 each branch), then softmax(q k^T / sqrt(D)) v over positions
-//                 0 .. pos[b] for the G query heads (online softmax over
-//                 chunks of 256 positions).
+//   attention split (b, h, j): waits on E_qk[i] (wait count 2: one notify
+//                 from each branch), then the online softmax of the G query
+//                 heads over its share of positions 0 .. pos[b] (split j of NS
+//                 equal ranges of the cache, chunks of 256 positions): running
+//                 max, sum and unnormalised output to the workspace; notifies
+//                 E_att[i] (wait count NS);
+//   merge         (b, h): after E_att[i], out = sum_j e^(m_j - M) o_j /
+//                 sum_j e^(m_j - M) l_j with M = max_j m_j.
+// Splitting the positions puts NS workgroups on each (sequence, head): at a
+// batch of one sequence the attention is a chain of memory latencies, and a
+// single workgroup per head walked 600 positions in 110 us.
 // Static and dynamic schedules interleave the two branches' tasks (ids 2i,
 // 2i + 1), so they run at the same time on different compute units; the
 // barrier baseline runs them as two operators with a global event between
@@ -32,17 +39,22 @@ struct DecodeArgs {
   uint16_t* kc;         // [B, S, Hk, D] key cache
   uint16_t* vc;         // [B, S, Hk, D] value cache
   float* qr;            // [B, Hq, D] rotated queries (workspace)
+  float* po;            // [B * Hk, NS, G, D] split partial outputs (workspace)
+  float* pml;           // [B * Hk, NS, G, 2] split running max and sum (workspace)
   float* out;           // [B, Hq, D]
   int B, Hq, Hk, S, G;
+  int NS, L;            // attention splits per (sequence, head), positions per split
   float theta_log2;     // log2 of the RoPE base
   float eps;
   int ev_qk;            // E_qk[b * Hk + h]
+  int ev_att;           // E_att[b * Hk + h]
 };
 
 constexpr int kHeadDim = 128;         // D: lane l holds elements l and l + 64
 constexpr int kMaxGroup = 16;         // G = Hq / Hk
 constexpr int kAttnChunk = kThreads;  // positions per online-softmax chunk
-enum : int { EV_QALL = 0, EV_KALL = 1, EV_DEC_FIXED = 8 };
+constexpr int kMaxSplits = 8;         // attention splits per (sequence, head)
+enum : int { EV_QALL = 0, EV_KALL = 1, EV_ATT = 2, EV_DEC_FIXED = 8 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
@@ -100,7 +112,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
   };
 
   // both branches notify E_qk[i]; the second one fires it (dynamic: it
-  // pushes the attention task)
+  // pushes the attention splits of (b, h))
   auto branch_done = [&](int i, int task, int op_event) ET_INLINE {
     if (sched == ET_SCHED_PER_OP) return;
     wg_release();
@@ -109,7 +121,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
     } else if (sched == ET_SCHED_STATIC) {
       t0_notify(c, a.ev_qk + i, 1, 2, task);
     } else if (wg_notify(c, a.ev_qk + i, 1, 2, task)) {
-      wg_push(c, 1, [&](int) { return 2 * N + i; }, [&](int) { return i; });
+      wg_push(c, a.NS, [&](int j) { return 2 * N + i * a.NS + j; },
+              [&](int j) { return i * a.NS + j; });
     }
   };
 
@@ -147,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
     return true;
   };
 
-  auto attention = [&](int i, int task) ET_INLINE -> bool {
+  auto attention = [&](int i, int split, int task) ET_INLINE -> bool {
     const int b = i / a.Hk, h = i % a.Hk;
     if (sched == ET_SCHED_STATIC) {
       if (!wg_wait(c, a.ev_qk + i, 2, task)) return false;
@@ -157,6 +170,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
     const int p = seq_pos(b, task);
     if (p < 0) return false;
     const int n = p + 1;
+    const int p0 = split * a.L, p1 = min(n, p0 + a.L);   // this split's positions
     const float scale = 1.0f / __builtin_sqrtf((float)kHeadDim);
     const size_t q0 = ((size_t)b * a.Hq + h * G) * kHeadDim;
     for (int x = tid; x < G * kHeadDim; x += kThreads) qs[x / kHeadDim][x % kHeadDim] = ld_coh(&a.qr[q0 + x]);
@@ -178,10 +192,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
     // memory latency on every position).
     const int qlast = n - 1;
     const Rsrc rv = make_rsrc(a.vc + base, (uint32_t)((size_t)n * rstride * 2));
-    for (int c0 = 0; c0 < n; c0 += kAttnChunk) {
+    for (int c0 = p0; c0 < p1; c0 += kAttnChunk) {
       // scores of position c0 + tid for every head of the group
       const int pp = c0 + tid;
-      const uint32_t off = pp < n ? (uint32_t)(pp * rstride * 2) : kOOB;
+      const uint32_t off = pp < p1 ? (uint32_t)(pp * rstride * 2) : kOOB;
       i32x4 kr[kHeadDim / 8];
       if (pp == qlast) {
 #pragma unroll
@@ -210,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
                     qb.x * kf[4] + qb.y * kf[5] + qb.z * kf[6] + qb.w * kf[7];
           }
       }
-      for (int g = 0; g < G; ++g) sc[g][tid] = pp < n ? s[g] * scale : -__builtin_inff();
+      for (int g = 0; g < G; ++g) sc[g][tid] = pp < p1 ? s[g] * scale : -__builtin_inff();
       __syncthreads();
       // online softmax: wave w updates the running max and sum of heads w, w+4, ...
       for (int g = wave; g < G; g += 4) {
@@ -241,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
           o[g][0] *= alpha[g];
           o[g][1] *= alpha[g];
         }
-      const int cend = min(n, c0 + kAttnChunk);
+      const int cend = min(p1, c0 + kAttnChunk);
       const int vend = min(cend, qlast);       // input rows (plain loads)
       auto add_row = [&](int q, uint32_t two) ET_INLINE {
         const float v0 = __builtin_bit_cast(float, two << 16);
@@ -279,9 +293,57 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
         part[wave][g][2 * dp + 1] = o[g][1];
       }
     __syncthreads();
+    const size_t ps = (size_t)i * a.NS + split;          // this split's partial
     for (int x = tid; x < G * kHeadDim; x += kThreads) {
       const int g = x / kHeadDim, d = x % kHeadDim;
-      const float v = ((part[0][g][d] + part[1][g][d]) + part[2][g][d]) + part[3][g][d];
+      st_coh(&a.po[ps * G * kHeadDim + x], ((part[0][g][d] + part[1][g][d]) + part[2][g][d]) + part[3][g][d]);
+    }
+    if (tid < G) {
+      st_coh(&a.pml[(ps * G + tid) * 2], m_run[tid]);
+      st_coh(&a.pml[(ps * G + tid) * 2 + 1], l_run[tid]);
+    }
+    if (sched == ET_SCHED_PER_OP) return true;
+    wg_release();
+    if (sched == ET_SCHED_BARRIER) {
+      t0_notify_bcast(c, EV_ATT, EV_ATT, 1, N * a.NS, task);
+    } else if (sched == ET_SCHED_STATIC) {
+      t0_notify(c, a.ev_att + i, 1, a.NS, task);
+    } else if (wg_notify(c, a.ev_att + i, 1, a.NS, task)) {
+      wg_push(c, 1, [&](int) { return 2 * N + N * a.NS + i; }, [&](int) { return i; });
+    }
+    return true;
+  };
+
+  // merge of the NS splits of (b, h): the splits' running maxima rescale
+  // their sums and outputs to the largest one (splits past the sequence's
+  // length hold max -inf and contribute nothing)
+  auto merge = [&](int i, int task) ET_INLINE -> bool {
+    if (sched == ET_SCHED_STATIC) {
+      if (!wg_wait(c, a.ev_att + i, a.NS, task)) return false;
+    } else if (sched == ET_SCHED_BARRIER) {
+      if (!wg_wait_bcast(c, EV_ATT, EV_ATT, task)) return false;
+    }
+    const int b = i / a.Hk, h = i % a.Hk;
+    const size_t q0 = ((size_t)b * a.Hq + h * G) * kHeadDim;
+    if (tid < G) {
+      float M = -__builtin_inff();
+      for (int j = 0; j < a.NS; ++j) M = fmaxf(M, ld_coh(&a.pml[(((size_t)i * a.NS + j) * G + tid) * 2]));
+      float l = 0.f;
+      for (int j = 0; j < a.NS; ++j) {
+        const size_t q = ((size_t)i * a.NS + j) * G + tid;
+        const float mj = ld_coh(&a.pml[q * 2]);
+        const float w = mj == -__builtin_inff() ? 0.f : __expf(mj - M);
+        l += w * ld_coh(&a.pml[q * 2 + 1]);
+        sc[tid][j] = w;
+      }
+      l_run[tid] = l;
+    }
+    __syncthreads();
+    for (int x = tid; x < G * kHeadDim; x += kThreads) {
+      const int g = x / kHeadDim;
+      float v = 0.f;
+      for (int j = 0; j < a.NS; ++j)
+        v += sc[g][j] * ld_coh(&a.po[((size_t)i * a.NS + j) * G * kHeadDim + x]);
       a.out[q0 + x] = v / l_run[g];
     }
     __syncthreads();
@@ -291,13 +353,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
   // task -> (kind, i): static / dynamic interleave the branches (2i query,
   // 2i + 1 key); the baselines run all query tasks, then all key tasks
   auto run = [&](int t) ET_INLINE -> bool {
-    if (t >= 2 * N) return attention(t - 2 * N, t);
+    if (t >= 2 * N + N * a.NS) return merge(t - 2 * N - N * a.NS, t);
+    if (t >= 2 * N) return attention((t - 2 * N) / a.NS, (t - 2 * N) % a.NS, t);
     const int i = interleaved ? t >> 1 : t % N;
     const bool key = interleaved ? (t & 1) != 0 : t >= N;
     return key ? key_branch(i, t) : query_branch(i, t);
   };
 
-  const int total = 3 * N;
+  const int total = 2 * N + N * a.NS + N;
   if (sched == ET_SCHED_DYNAMIC) {
     bool ok = true;
     for (int t = c.wg; ok && t < ra.init_base; t += c.G) {
@@ -315,7 +378,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
       trace_task(c, t, t0);
     }
   } else if (sched == ET_SCHED_PER_OP) {
-    const int lo = ra.phase * N, hi = lo + N;
+    // phases: query branch, key branch, attention splits, merges
+    const int bounds[5] = {0, N, 2 * N, 2 * N + N * a.NS, 2 * N + N * a.NS + N};
+    const int lo = bounds[ra.phase], hi = bounds[ra.phase + 1];
     for (int t = lo + c.wg; t < hi; t += c.G) {
       const long long t0 = trace_now(c);
       if (!run(t)) break;
@@ -348,6 +413,17 @@ int launch_decode(const LaunchCommon& lc, const uint16_t* q, const uint16_t* k,
   a.kc = kc;
   a.vc = vc;
   a.qr = reinterpret_cast<float*>(lc.ws + p->off_aux);
+  // splits: enough ranges of the cache (a multiple of 64 positions each, at
+  // most kMaxSplits) that the (sequence, head) pairs times the splits give
+  // every workgroup a task; with as many pairs as workgroups, one split
+  const int pairs = B * p->n_kv_heads;
+  const int want = min(kMaxSplits, max(1, lc.G / pairs));
+  const int L = cdiv(cdiv(S, want), 64) * 64;
+  a.NS = cdiv(S, L);
+  a.L = L;
+  const size_t qr_floats = (size_t)p->max_tokens * p->n_heads * kHeadDim;
+  a.po = a.qr + qr_floats;
+  a.pml = a.po + kMaxSplits * qr_floats;
   a.out = out;
   a.B = B;
   a.Hq = p->n_heads;
@@ -356,16 +432,17 @@ int launch_decode(const LaunchCommon& lc, const uint16_t* q, const uint16_t* k,
   a.G = a.Hq / a.Hk;
   a.theta_log2 = (float)__builtin_log2((double)theta);
   a.eps = eps;
-  a.ev_qk = EV_DEC_FIXED;
   const int N = B * a.Hk;
+  a.ev_qk = EV_DEC_FIXED;
+  a.ev_att = EV_DEC_FIXED + N;
   RunArgs ra = lc.run_args();
   ra.init_base = 2 * N < lc.G ? 2 * N : lc.G;   // dynamic: the first round of branch tasks runs directly
   ra.n_init = 2 * N - ra.init_base;              // the rest are implicit queue entries
-  ra.total_hint = 3 * N - ra.init_base;          // queue tasks: those and the pushed attention tasks
-  ra.extent = EV_DEC_FIXED + N;
+  ra.total_hint = 2 * N + N * a.NS + N - ra.init_base;   // queue tasks: those and the pushed ones
+  ra.extent = EV_DEC_FIXED + 2 * N;
   const void* kern = reinterpret_cast<const void*>(&decode_kernel);
   if (lc.sched == ET_SCHED_PER_OP) {
-    for (int ph = 0; ph < 3; ++ph) {
+    for (int ph = 0; ph < 4; ++ph) {
       ra.phase = ph;
       const int e = lc.launch(kern, &ra, &a, false);
       if (e) return e;

@@ -20,7 +20,7 @@ SCHED_STATIC, SCHED_DYNAMIC, SCHED_BARRIER, SCHED_PER_OP = 0, 1, 2, 3
 SCHEDS = {"static": 0, "dynamic": 1, "barrier": 2, "per_op": 3}
 OK, EINVAL, EWORKSPACE, EHIP, ETIMEOUT, EUNSUPPORTED, ESTATE, ERANGE = range(8)
 WL_SPLITK, WL_MLP, WL_MOE, WL_BLOCK, WL_DECODE = 1, 2, 3, 4, 5
-DEBUG_COUNTS, DEBUG_TRACE, SCRATCH_RESET = 1, 2, 4
+DEBUG_COUNTS, DEBUG_TRACE, SCRATCH_RESET, DEBUG_WATCHDOG_TICK = 1, 2, 4, 8
 
 c_int, c_size_t, c_void_p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 

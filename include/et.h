@@ -77,8 +77,11 @@ enum { ET_WL_SPLITK = 1, ET_WL_MLP = 2, ET_WL_MOE = 3, ET_WL_BLOCK = 4, ET_WL_DE
 enum {
   ET_DEBUG_COUNTS = 1,  /* count how many times each task ran (et_layout.runs) */
   ET_DEBUG_TRACE = 2,   /* record each task's workgroup and start / end time (et_layout.trace) */
-  ET_SCRATCH_RESET = 4  /* et_moe_layer_noalloc only: clear the library-held scratch state (event
+  ET_SCRATCH_RESET = 4, /* et_moe_layer_noalloc only: clear the library-held scratch state (event
                            counters, ready queue, sticky fault word) before this call */
+  ET_DEBUG_WATCHDOG_TICK = 8  /* watchdog of one 10 ns clock tick instead of timeout_ms: a wait
+                                 that is still pending at its first watchdog check ends the call
+                                 with ET_ETIMEOUT (tests of the timeout path) */
 };
 
 /* Launch modes of the persistent kernels.  Every workgroup of a persistent

@@ -102,18 +102,28 @@ def test_decode_schedules_bit_identical():
 @pytest.mark.parametrize("sched", ["static", "dynamic"])
 def test_decode_event_invariants(sched):
     """Every task ran once; every E_qk event received its two notifies (one
-    from each branch)."""
-    B, Hq, Hk = 24, 64, 8
+    from each branch) and every E_att event one per attention split (24
+    sequences x 8 heads = 192 pairs on 256 workgroups: one split; 2
+    sequences: 16 pairs, 8 splits of 128 positions)."""
+    for B, NS in ((24, 1), (2, 8)):
+        _invariants(B, NS, sched)
+
+
+def _invariants(B, NS, sched):
+    Hq, Hk = 64, 8
+    assert et.num_workers() == 256
     ws = _ws(Hq, Hk)
     ws.runs().zero_()
     inp, res = run(B, Hq, Hk, sched, debug=et.DEBUG_COUNTS)
     st = ws.status()
     N = B * Hk
+    total = 2 * N + N * NS + N
     runs = ws.runs().cpu().numpy()
-    assert st["last_tasks"] == 3 * N
-    assert (runs[:3 * N] == 1).all() and (runs[3 * N:] == 0).all()
+    assert st["last_tasks"] == total
+    assert (runs[:total] == 1).all() and (runs[total:] == 0).all()
     cnt = ws.counters(1 - st["bank"]).cpu().numpy()
-    assert (cnt[8:8 + N] == -2).all() and (cnt[:8] == 0).all()
+    assert (cnt[8:8 + N] == -2).all() and (cnt[8 + N:8 + 2 * N] == -NS).all()
+    assert (cnt[:8] == 0).all()
     check(inp, res)
 
 

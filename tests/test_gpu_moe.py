@@ -371,3 +371,26 @@ def test_central_queue(T):
     _, _, _, _, out1, aux1, _ = run_moe("moe_skewed", T, "dynamic", queue_shards=1)
     assert np.array_equal(out8, out1)
     check_against_oracle("moe_skewed", T, out1, aux1)
+
+
+@pytest.mark.parametrize("sched", ["static", "dynamic", "barrier"])
+def test_watchdog_timeout_is_reported(sched):
+    """A one-tick watchdog (forced from the host) makes the first wait still
+    pending at its check end the call: the device records ET_ETIMEOUT, every
+    workgroup leaves (the call completes), later calls do nothing until the
+    workspace is re-initialised, and then the layer matches the oracle again."""
+    ws = et.Workspace(et.WL_MOE, 1024, 2048, 768, 128, 8, device=DEV)
+    cfg, logits, x, (wg, wu, wd), _, _, _ = run_moe("moe_skewed", 1024, sched, ws=ws)
+    out = torch.zeros((1024, cfg["hidden"]), device=DEV)
+    say("moe watchdog tick", sched)
+    et.moe_layer(logits, x, wg, wu, wd, out, ws, sched, debug=et.DEBUG_WATCHDOG_TICK)
+    torch.cuda.synchronize()
+    st = ws.status()
+    assert st["status"] == et.ETIMEOUT, st
+    calls = st["calls"]
+    et.moe_layer(logits, x, wg, wu, wd, out, ws, sched)       # sticky: no work done
+    torch.cuda.synchronize()
+    assert ws.status()["status"] == et.ETIMEOUT and ws.status()["calls"] == calls
+    ws.init()
+    _, _, _, _, out2, aux, _ = run_moe("moe_skewed", 1024, sched, ws=ws)
+    check_against_oracle("moe_skewed", 1024, out2, aux)
