@@ -238,6 +238,67 @@ def ceilings():
     print(json.dumps(res))
 
 
+def weight_copies(args, nbytes):
+    """Copies of a weight set to rotate so that one rotation streams at least
+    1 GiB (none without --cold, or when one copy already exceeds 1 GiB)."""
+    if not args.cold or nbytes >= (1 << 30):
+        return 1
+    return -(-(1 << 30) // nbytes)
+
+
+def bench_dense(args):
+    """The split-K example (2048 rows x 128) and the dense MLP (hidden 2048,
+    intermediate 5632, batch --tokens): time per call under every schedule,
+    the algorithmic bytes against HBM; --cold rotates weight copies."""
+    import torch
+    from event_driven_moe_amd import et, synth
+    dev = "cuda"
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    turn = [0]
+    if args.workload == "splitk":
+        rows = 2048
+        A = synth.splitk_inputs(rows, device=dev)
+        Bp = torch.empty((rows, 4), device=dev)
+        C = torch.empty(rows, device=dev)
+        ws = et.Workspace(et.WL_SPLITK, rows, device=dev)
+        call = lambda s: et.splitk_reduce(A, Bp, C, ws, s)
+        nbytes = rows * 128 * 4 + 2 * rows * 4 * 4 + rows * 4
+        flops = rows * 127
+        desc = "split-K reduction example, A fp32 (2048, 128), 64 events x 4 stage-1 tiles"
+        ncopies = 1
+    else:
+        B, H, I = args.tokens, 2048, 5632
+        x, wg, wu, wd = synth.mlp_inputs(B, H, I, device=dev)
+        w = (synth.k_major(wg), synth.k_major(wu), synth.k_major(wd))
+        copies = [w] + [tuple(t.clone() for t in w)
+                        for _ in range(weight_copies(args, 3 * H * I * 2) - 1)]
+        ncopies = len(copies)
+        y = torch.empty((B, H), device=dev)
+        ws = et.Workspace(et.WL_MLP, B, H, I, device=dev)
+
+        def call(s):
+            g, u, d = copies[turn[0] % len(copies)]
+            turn[0] += 1
+            et.mlp(x, g, u, d, y, ws, s)
+        nbytes = 3 * H * I * 2 + B * H * 2 + B * H * 4
+        flops = 2 * 3 * H * I * B
+        desc = ("dense SiLU-gated MLP, hidden 2048, intermediate 5632, batch %d, %s" %
+                (B, "cold (%d weight copies rotated)" % ncopies if ncopies > 1 else "warm"))
+    modes = {}
+    for s in ("static", "dynamic", "barrier", "per_op"):
+        log("bench: %s %s" % (args.workload, s))
+        p, _ = time_calls(lambda: call(s), args.steps, args.warmup)
+        modes[s] = round(1e3 * sum(p) / len(p), 2)
+    if ws.status()["status"] != 0:
+        raise SystemExit("device fault: %s" % ws.status())
+    best = min(modes.values())
+    print(json.dumps({"workload": desc, "tokens": args.tokens if args.workload == "mlp" else 2048,
+                      "us_per_call_by_schedule": modes, "algorithmic_bytes": nbytes,
+                      "flops": flops, "weight_copies_rotated": ncopies,
+                      "hbm_frac_best": round(nbytes / (best * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                      "mfma_frac_best": round(flops / (best * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS, 4)}))
+
+
 def bench_chain(args):
     """The router GEMM -> MoE -> dense MLP chain (et_moe_block) or the decode
     attention front (et_decode_attention): time per call under every
@@ -312,6 +373,9 @@ def main():
     ap.add_argument("--no-modes", action="store_true",
                     help="time only --sched (default: every schedule, reported in config)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cold", action="store_true",
+                    help="rotate copies of the weights (>= 1 GiB in total) from call to call, so "
+                         "that no call finds its weights in the 256 MB Infinity Cache")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy before timing (reference for HBM counters)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
@@ -335,6 +399,9 @@ def main():
     if args.workload.startswith("block_") or args.workload == "decode":
         bench_chain(args)
         return
+    if args.workload in ("splitk", "mlp"):
+        bench_dense(args)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -353,9 +420,14 @@ def main():
     ws = et.Workspace(et.WL_MOE, T, cfg["hidden"], cfg["inter"], cfg["n_experts"],
                       cfg["top_k"], device=dev)
     out = torch.empty((T, cfg["hidden"]), device=dev)
+    copies = [(wg, wu, wd)] + [(wg.clone(), wu.clone(), wd.clone())
+                               for _ in range(weight_copies(args, 3 * wg.numel() * 2) - 1)]
+    turn = [0]
 
     def step(sched=args.sched):
-        et.moe_layer(logits, x, wg, wu, wd, out, ws, sched, fetch_batch=args.fetch)
+        g, u, d = copies[turn[0] % len(copies)]
+        turn[0] += 1
+        et.moe_layer(logits, x, g, u, d, out, ws, sched, fetch_batch=args.fetch)
 
     step()
     torch.cuda.synchronize()
@@ -436,6 +508,12 @@ def main():
             "mfma_frac": round(achieved_tfs / MFMA_BF16_PEAK_TFS, 4),
             "hbm_frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
             "kernel": "moe_kernel (one persistent launch per layer)",
+            "weight_copies_rotated": len(copies),
+            "cache_state": ("cold: %d weight copies rotated call to call" % len(copies)
+                            if len(copies) > 1 else
+                            "weights far larger than the 256 MB Infinity Cache"
+                            if 3 * wg.numel() * 2 > (1 << 30) else
+                            "warm: one weight copy, re-read every call"),
         },
         "roofline": roof,
     }

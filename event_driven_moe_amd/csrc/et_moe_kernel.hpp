@@ -95,6 +95,9 @@ constexpr int kGenRowsOff = 0, kGenFired = 512, kGenIdx = 1024;
 // cost as much as they save, and at 64 tokens (64-row blocks) far more
 // (moe_skewed T=64 static 94 -> 115 us).
 constexpr int kInlineCombineTokens = 4;
+// Dynamic schedule: with at most this many gate/up tasks per workgroup, routing
+// chunk 0 alone pushes them (early push); with more, every chunk pushes a share.
+constexpr int kSoloPush = 4;
 constexpr int kIdxCache = 2 * (kMaxExperts + 1) * 4;   // tok_indptr + blk_indptr copies
 constexpr int kGenBytes = kGenIdx + kIdxCache;
 
@@ -881,7 +884,11 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       // blocks (a data-dependent wait count); the notify that completes it
       // pushes all of the expert's down tasks, in (column tile, block) order,
       // so the blocks sharing a weight tile are claimed together from one
-      // shard and stream that tile through the XCD's L2 once
+      // shard and stream that tile through the XCD's L2 once.  (Pushing the
+      // down tasks early instead, behind every gate/up task, was slower:
+      // 257 us against 204 on moe_skewed T=1024 -- an early-pushed task takes
+      // its queue slot in a fixed order and its worker waits for its block,
+      // while tasks pushed on completion enter the queue ready to run.)
       const int nblk = c_blk[e + 1] - c_blk[e];
       if (wg_notify(c, m.ev_he + e, 1, nblk * nt1, task)) {
         // block-major push order: a shard holds (block 0: its tiles), (block 1:
@@ -1212,34 +1219,42 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
         // E_exp event, so the weight stream overlaps the grouping.  The
         // pushed tasks read the offsets and totals chunk 0 publishes before
         // EV_SCAN (few chunks: this chunk published them itself).
+        // Up to kSoloPush tasks per workgroup, chunk 0 pushes them all and the
+        // other chunks go straight to their grouping: a chunk that pushes
+        // first waits for EV_SCAN, and with a few tasks each that wait and the
+        // push itself put 10 us on the front (moe_skewed T=1024: the front
+        // ended at 28.9 us against the static schedule's 19.1 us).
         if (task == 0) set_total(c, nb * (nt1 + nt2) + ncomb + (kBlock ? n_mg + n_md : 0));
-        wg_release();
-        if (task != 0 && many_chunks && !wg_wait_bcast(c, EV_SCAN, EV_SCAN, task)) return false;
-        const int* blk = reinterpret_cast<const int*>(s1) + 1024;   // exclusive block offsets
         const int total1 = nb * nt1;
-        const int j0 = (int)((long long)task * total1 / NR);
-        const int j1 = (int)((long long)(task + 1) * total1 / NR);
-        // gate/up task j of the push order (experts ascending, block-major
-        // within an expert) -> expert holding it: the largest e whose first
-        // task is <= j (experts without rows share their successor's start)
-        auto expert_of = [&](int j) ET_INLINE {
-          int lo = 0, hi = m.E;
-          while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (blk[mid] * nt1 <= j) lo = mid; else hi = mid;
-          }
-          return lo;
-        };
-        auto nblk_of = [&](int e) ET_INLINE { return (e + 1 < m.E ? blk[e + 1] : nb) - blk[e]; };
-        wg_push(c, j1 - j0,
-                [&](int i) {
-                  const int j = j0 + i, e = expert_of(j), l = j - blk[e] * nt1;
-                  return base1 + blk[e] * nt1 + (l % nt1) * nblk_of(e) + l / nt1;
-                },
-                [&](int i) {
-                  const int j = j0 + i, e = expert_of(j);
-                  return tile_key(e, (j - blk[e] * nt1) % nt1, nt1);
-                });
+        const bool solo_push = total1 <= kSoloPush * c.G;
+        if (!solo_push || task == 0) {
+          wg_release();
+          if (task != 0 && many_chunks && !wg_wait_bcast(c, EV_SCAN, EV_SCAN, task)) return false;
+          const int* blk = reinterpret_cast<const int*>(s1) + 1024;   // exclusive block offsets
+          const int j0 = solo_push ? 0 : (int)((long long)task * total1 / NR);
+          const int j1 = solo_push ? total1 : (int)((long long)(task + 1) * total1 / NR);
+          // gate/up task j of the push order (experts ascending, block-major
+          // within an expert) -> expert holding it: the largest e whose first
+          // task is <= j (experts without rows share their successor's start)
+          auto expert_of = [&](int j) ET_INLINE {
+            int lo = 0, hi = m.E;
+            while (hi - lo > 1) {
+              const int mid = (lo + hi) >> 1;
+              if (blk[mid] * nt1 <= j) lo = mid; else hi = mid;
+            }
+            return lo;
+          };
+          auto nblk_of = [&](int e) ET_INLINE { return (e + 1 < m.E ? blk[e + 1] : nb) - blk[e]; };
+          wg_push(c, j1 - j0,
+                  [&](int i) {
+                    const int j = j0 + i, e = expert_of(j), l = j - blk[e] * nt1;
+                    return base1 + blk[e] * nt1 + (l % nt1) * nblk_of(e) + l / nt1;
+                  },
+                  [&](int i) {
+                    const int j = j0 + i, e = expert_of(j);
+                    return tile_key(e, (j - blk[e] * nt1) % nt1, nt1);
+                  });
+        }
       }
       ts = trace_now(c);
       group_chunk(task);
