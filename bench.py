@@ -369,7 +369,7 @@ def main():
     ap.add_argument("--workload", default="moe_large")
     ap.add_argument("--tokens", type=int, default=8192)
     ap.add_argument("--sched", default="static")
-    ap.add_argument("--fetch", type=int, default=4)
+    ap.add_argument("--fetch", type=int, default=2)
     ap.add_argument("--no-modes", action="store_true",
                     help="time only --sched (default: every schedule, reported in config)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")

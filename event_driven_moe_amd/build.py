@@ -23,6 +23,11 @@ CFLAGS = [
     "-munsafe-fp-atomics",
     # packed fp32 instructions stay off: scalar / float2 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no wave-aggregated atomics: every atomic here is issued by one lane (or
+    # at per-item addresses), and the aggregated form reads its result back
+    # at once, which would put the queue claim's round trip on the path the
+    # claim-ahead takes it off
+    "-Xarch_device", "-mllvm=-amdgpu-atomic-optimizer-strategy=None",
     "-I" + os.path.join(ROOT, "include"),
     "-Wno-unused-result",
 ]

@@ -77,8 +77,8 @@ int fill_common(LaunchCommon& lc, void* ws, const et_plan* plan, int sched, cons
   lc.plan = plan;
   lc.ws = static_cast<char*>(ws);
   lc.sched = sched;
-  lc.fetch = o && o->fetch_batch > 0 ? o->fetch_batch : 4;
-  if (lc.fetch > 8) return ET_EINVAL;
+  lc.fetch = o && o->fetch_batch > 0 ? o->fetch_batch : 2;
+  if (lc.fetch > kMaxFetch) return ET_EINVAL;
   lc.debug = o ? o->debug_flags : 0;
   lc.timeout_ms = o && o->timeout_ms > 0 ? o->timeout_ms : 2000;
   lc.tile = o ? o->tile : -1;

@@ -87,8 +87,11 @@ struct RunArgs {
 };
 
 // Workgroup-shared scratch for broadcasts and keyed pushes.
+constexpr int kMaxFetch = 8;   // largest claim batch (fetch_batch)
+
 struct Shared {
   int v[8];
+  int bids[kMaxFetch];    // pop: the slot values of the claimed batch, read together
   int qn[kMaxShards];     // push: tasks per shard, then slots filled so far
   int qb[kMaxShards];     // push: first slot per shard
   int wq[kThreads / 64][kMaxShards];   // push: items per wave and shard in a round
@@ -392,6 +395,10 @@ struct PopState {
   int base = 0;
   int size = 0;
   int left = 0;
+  bool ahead = false;    // claim the next batch before running this one's last task
+  int pre_base = 0;      // that claim's first index (its atomic's return value)
+  int pre_size = 0;      // its size; 0: none outstanding
+  int pre_pushed = 0;    // the shard's push counter read beside that atomic
 };
 
 // Implicit initial tasks of shard q: ids q, q + nq, ... below n_init.
@@ -456,25 +463,72 @@ __device__ __forceinline__ int resolve_slot(const Ctx& c, int q, int idx) {
 // published beyond the claim counter, so a worker never holds published
 // tasks while others idle; short leading phases are claimed one slot at a
 // time.  A racy peek is enough: any claim size is correct.
+//
+// Latency: the slots of a batch are read in one memory round trip when it is
+// claimed, and while the shard holds at least three rounds of full batches
+// for every worker beyond the claim counter, the next batch's atomic is
+// issued before the current batch's last task runs and its result is first
+// used at the next pop -- the claim round trips then overlap that task's own
+// first loads instead of sitting between tasks.  (moe_large T=8192, dynamic:
+// median / 90th percentile gap between a worker's tasks 1.08 / 2.4 us
+// before, 0.88 / 2.0 us after; what remains is the batch's slot read and
+// the claims made while the shard holds little queued work.)  Holding the next batch early cannot deadlock: a shard is FIFO,
+// a worker claims from its own shard only, and in every workload here a
+// claimed task waits only on tasks queued before it (or on no queued task).
 __device__ __forceinline__ int wg_pop(const Ctx& c, PopState& ps) {
   int t = -1;
   if (threadIdx.x == 0) {
     const RunArgs& a = c.a;
     const int q = c.wg % a.nq;
+    const int n_init = shard_init(a, q);
+    int* head = q_claimed(a, q);
     if (ps.left == 0) {
-      int* head = q_claimed(a, q);
-      const int h = ld_rlx(head);
-      const int avail = shard_init(a, q) + ld_rlx(q_pushed(a, q)) - h;
-      const int per = c.G / a.nq;
-      int sz = avail / (per > 0 ? per : 1);
-      sz = h * a.nq < a.n_single ? 1 : (sz < 1 ? 1 : (sz > a.fetch ? a.fetch : sz));
-      ps.base = add_rlx(head, sz);
-      ps.size = ps.left = sz;
+      if (ps.pre_size > 0) {
+        ps.base = ps.pre_base;
+        ps.size = ps.left = ps.pre_size;
+        ps.pre_size = 0;
+        const int per = c.G / a.nq > 0 ? c.G / a.nq : 1;
+        ps.ahead = n_init + ps.pre_pushed - (ps.base + ps.size) >= 3 * per * a.fetch;
+      } else {
+        const int h = ld_rlx(head);
+        const int avail = n_init + ld_rlx(q_pushed(a, q)) - h;
+        const int per = c.G / a.nq > 0 ? c.G / a.nq : 1;
+        int sz = avail / per;
+        sz = h * a.nq < a.n_single ? 1 : (sz < 1 ? 1 : (sz > a.fetch ? a.fetch : sz));
+        ps.ahead = sz == a.fetch && avail >= 3 * per * a.fetch;
+        ps.base = add_rlx(head, sz);
+        ps.size = ps.left = sz;
+      }
+      int v[kMaxFetch];
+#pragma unroll
+      for (int i = 0; i < kMaxFetch; ++i) {
+        const int sl = ps.base + i - n_init;
+        v[i] = (i < ps.size && sl >= 0 && sl < a.q_cap) ? ld_rlx(&a.slots[(size_t)q * a.q_cap + sl]) : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < kMaxFetch; ++i)
+        if (i < ps.size) c.sh->bids[i] = v[i];
     }
-    const int idx = ps.base + (ps.size - ps.left);
+    const int k = ps.size - ps.left;
+    const int idx = ps.base + k;
     --ps.left;
-    t = resolve_slot(c, q, idx);
-    if (t < 0) t = -1;
+    if (idx < n_init) {
+      t = a.init_base + q + a.nq * idx;
+    } else {
+      const int v = c.sh->bids[k];
+      if (v != 0) {
+        st_rlx(&a.slots[(size_t)q * a.q_cap + (idx - n_init)], 0);   // empty for the next call
+        t = v - 1;
+      } else {
+        t = resolve_slot(c, q, idx);   // not yet written when read: wait for it
+        if (t < 0) t = -1;
+      }
+    }
+    if (ps.left == 0 && ps.ahead && t >= 0) {
+      ps.pre_base = add_rlx(head, a.fetch);
+      ps.pre_pushed = ld_rlx(q_pushed(a, q));
+      ps.pre_size = a.fetch;
+    }
   }
   return wg_bcast(c, t, 4);
 }

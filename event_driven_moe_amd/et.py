@@ -149,7 +149,7 @@ def _ptr(t, dtype, name, shape=None):
 LAUNCH_ORDINARY, LAUNCH_COOPERATIVE = 0, 1
 
 
-def _opts(fetch_batch=4, debug=0, timeout_ms=2000, tile=-1, cooperative=False, queue_shards=0):
+def _opts(fetch_batch=2, debug=0, timeout_ms=2000, tile=-1, cooperative=False, queue_shards=0):
     return Opts(fetch_batch, debug, timeout_ms, tile,
                 LAUNCH_COOPERATIVE if cooperative else LAUNCH_ORDINARY, queue_shards)
 

@@ -100,7 +100,7 @@ enum {
 
 /* Per-call options; pass NULL for the defaults. */
 typedef struct et_opts {
-  int fetch_batch;   /* dynamic mode: queue slots claimed per atomic (1..8; default 4) */
+  int fetch_batch;   /* dynamic mode: queue slots claimed per atomic (1..8; default 2) */
   int debug_flags;   /* ET_DEBUG_* (default 0) */
   int timeout_ms;    /* watchdog for every wait / queue spin (default 2000 ms) */
   int tile;          /* MoE / MLP tile-variant override (-1 = chosen from the token count) */
