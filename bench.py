@@ -211,11 +211,21 @@ def ceilings():
         return e0.elapsed_time(e1) / reps * 1e-3   # seconds per call
 
     out = torch.zeros(G * 4, device="cuda")
+    stamps = torch.zeros(G * 4, dtype=torch.int64, device="cuda")
     iters = 25000
-    t = timed(lambda: et.ceiling_mfma(out, iters), 5)
-    tf = G * 4 * iters * 32 * 16384 / t / 1e12
-    res["mfma_only_bf16"] = {"tflops": round(tf, 1), "frac_of_published": round(tf / MFMA_BF16_PEAK_TFS, 4),
-                             "ms": round(t * 1e3, 3)}
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    # operand sets: constants; normal(0, 1) bf16 values, as GEMM operands
+    # of a real layer would carry
+    for name, ops in (("const", None),
+                      ("randn", torch.randn(G * 256 * 16, generator=gen).to(torch.bfloat16).cuda())):
+        t = timed(lambda: et.ceiling_mfma(out, iters, operands=ops, stamps=stamps), 5)
+        st = stamps.view(G, 4).cpu().double()
+        ghz = float(((st[:, 2] - st[:, 0]) / (st[:, 3] - st[:, 1])).mean()) * 0.1
+        tf = G * 4 * iters * 32 * 16384 / t / 1e12
+        res["mfma_only_bf16_" + name] = {
+            "tflops": round(tf, 1), "frac_of_published": round(tf / MFMA_BF16_PEAK_TFS, 4),
+            "ms": round(t * 1e3, 3), "shader_clock_ghz": round(ghz, 3),
+            "frac_of_peak_at_that_clock": round(tf / (MFMA_BF16_PEAK_TFS * ghz / 2.4), 4)}
     buf = torch.empty(8 << 30, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
     for wpc in (2, 4, 8):
@@ -474,6 +484,17 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved_tfs / MFMA_BF16_PEAK_TFS, 4),
                 "traffic": traffic}
 
+    # the clock the timed schedule ran at: one more call recording each
+    # workgroup's real-time and shader-clock stamps at start and end
+    g, u, d = copies[0]
+    et.moe_layer(logits, x, g, u, d, out, ws, args.sched, fetch_batch=args.fetch,
+                 debug=et.DEBUG_CLOCK)
+    torch.cuda.synchronize()
+    stamps = ws.clock_stamps()[: et.num_workers()].cpu().long()
+    d_rt = (stamps[:, 1, 0] - stamps[:, 0, 0]) & 0xFFFFFFFF
+    d_sc = (stamps[:, 1, 1] - stamps[:, 0, 1]) & 0xFFFFFFFF
+    clock_ghz = float(d_sc.sum()) / float(d_rt.sum()) * 0.1 if int(d_rt.sum()) > 0 else None
+
     modes = {}
     if not args.no_modes:
         for s in ("static", "dynamic", "barrier", "per_op"):
@@ -508,6 +529,10 @@ def main():
             "mfma_frac": round(achieved_tfs / MFMA_BF16_PEAK_TFS, 4),
             "hbm_frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
             "kernel": "moe_kernel (one persistent launch per layer)",
+            "shader_clock_ghz": round(clock_ghz, 3) if clock_ghz else None,
+            "shader_clock_note": "mean clock over the workgroups of one call of the timed schedule "
+                                 "(shader clock counter against the 100 MHz real-time counter); the "
+                                 "published MFMA peak assumes 2.4 GHz",
             "weight_copies_rotated": len(copies),
             "cache_state": ("cold: %d weight copies rotated call to call" % len(copies)
                             if len(copies) > 1 else

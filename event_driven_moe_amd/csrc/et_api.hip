@@ -23,7 +23,9 @@ RunArgs LaunchCommon::run_args() const {
   a.q_cap = plan->max_tasks;
   a.nq = shards;
   a.runs = (debug & ET_DEBUG_COUNTS) ? reinterpret_cast<int*>(ws + plan->off_runs) : nullptr;
-  a.trace = (debug & ET_DEBUG_TRACE) ? reinterpret_cast<int*>(ws + plan->off_trace) : nullptr;
+  a.trace = (debug & (ET_DEBUG_TRACE | ET_DEBUG_CLOCK)) ? reinterpret_cast<int*>(ws + plan->off_trace)
+                                                       : nullptr;
+  a.trace_tasks = (debug & ET_DEBUG_TRACE) ? 1 : 0;
   a.sched = sched;
   a.fetch = fetch;
   a.phase = -1;
@@ -102,7 +104,7 @@ void finish_plan(et_plan* plan, size_t aux) {
   plan->off_runs = o;
   o = align_up(o + (size_t)plan->max_tasks * 4, 256);
   plan->off_trace = o;
-  o = align_up(o + (size_t)plan->max_tasks * 16 + 1024 * 8, 256);
+  o = align_up(o + (size_t)plan->max_tasks * 16 + 1024 * 16, 256);
   plan->off_aux = o;
   plan->aux_bytes = aux;
   plan->bytes = align_up(o + aux, 256);

@@ -20,12 +20,31 @@ namespace et {
 // to its own registers: with the builtin, the compiler moved the loop-carried
 // accumulators between registers every iteration (v_accvgpr moves and nops
 // between the MFMAs), which measured the moves, not the matrix unit.
-__global__ __launch_bounds__(kThreads, 1) void ceiling_mfma_kernel(float* out, int iters) {
+//
+// Operands: small constants (the same bits in every lane), or -- with `ops`
+// -- a fragment pair each lane loads from memory once (operand values decide
+// how much the matrix unit switches, and the device's clock under the load
+// follows its power).  `stamps`: per workgroup the shader clock counter and
+// the 100 MHz real-time counter at the start and at the end, so the clock
+// the loop ran at is their ratio.
+__global__ __launch_bounds__(kThreads, 1) void ceiling_mfma_kernel(const i32x4* ops, float* out,
+                                                                   long long* stamps, int iters) {
   const int lane = threadIdx.x & 63;
-  // small finite bf16 operands (exponent field well below all ones)
-  const int v = 0x3c003c00 + (lane << 2);
-  const i32x4 a = {v, v + 1, v + 2, v + 3};
-  const i32x4 b = {v + 4, v + 5, v + 6, v + 7};
+  i32x4 a, b;
+  if (ops) {
+    const size_t i = 2 * ((size_t)blockIdx.x * kThreads + threadIdx.x);
+    a = ops[i];
+    b = ops[i + 1];
+  } else {
+    // small finite bf16 operands (exponent field well below all ones)
+    const int v = 0x3c003c00 + (lane << 2);
+    a = i32x4{v, v + 1, v + 2, v + 3};
+    b = i32x4{v + 4, v + 5, v + 6, v + 7};
+  }
+  if (stamps && threadIdx.x == 0) {
+    stamps[4 * blockIdx.x] = __builtin_amdgcn_s_memtime();
+    stamps[4 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+  }
   f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, c2 = c0, c3 = c0, c4 = c0, c5 = c0, c6 = c0, c7 = c0;
   for (int it = 0; it < iters; ++it) {
     // four rounds of the eight chains per block; the leading nop covers the
@@ -49,6 +68,11 @@ __global__ __launch_bounds__(kThreads, 1) void ceiling_mfma_kernel(float* out, i
   // wait out the matrix pipeline's write latency explicitly
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   const f32x4 t = ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7));
+  __syncthreads();
+  if (stamps && threadIdx.x == 0) {
+    stamps[4 * blockIdx.x + 2] = __builtin_amdgcn_s_memtime();
+    stamps[4 * blockIdx.x + 3] = __builtin_amdgcn_s_memrealtime();
+  }
   if (lane == 0) out[blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)] = (t[0] + t[1]) + (t[2] + t[3]);
 }
 
@@ -72,11 +96,14 @@ using namespace et;
 
 extern "C" {
 
-int et_ceiling_mfma(float* out, int iters, hipStream_t stream) {
+int et_ceiling_mfma(const void* operands, float* out, long long* stamps, int iters,
+                    hipStream_t stream) {
   if (!out || iters <= 0) return ET_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(operands) & 15) != 0) return ET_EINVAL;
   const int g = et_num_workers();
   if (g < 0) return -g;
-  hipLaunchKernelGGL(ceiling_mfma_kernel, dim3(g), dim3(kThreads), 0, stream, out, iters);
+  hipLaunchKernelGGL(ceiling_mfma_kernel, dim3(g), dim3(kThreads), 0, stream,
+                     static_cast<const i32x4*>(operands), out, stamps, iters);
   return hipGetLastError() == hipSuccess ? ET_OK : ET_EHIP;
 }
 

@@ -74,7 +74,8 @@ struct RunArgs {
   int q_cap;
   int nq;              // ready-queue shards in use (1 or kMaxShards)
   int* runs;           // per-task run counts, or nullptr
-  int* trace;          // per-task trace records, or nullptr
+  int* trace;          // trace records (per workgroup, and per task if trace_tasks), or nullptr
+  int trace_tasks;     // record per-task trace entries
   int sched;           // ET_SCHED_*
   int fetch;           // dynamic: slots claimed per atomic
   int phase;           // per-op mode: operator this launch runs
@@ -539,10 +540,10 @@ __device__ __forceinline__ void count_run(const Ctx& c, int task) {
 
 // Debug trace: task -> (workgroup, start, end) in 100 MHz ticks.
 __device__ __forceinline__ long long trace_now(const Ctx& c) {
-  return c.a.trace ? now_ticks() : 0;
+  return c.a.trace && c.a.trace_tasks ? now_ticks() : 0;
 }
 __device__ __forceinline__ void trace_task(const Ctx& c, int task, long long t0) {
-  if (c.a.trace && threadIdx.x == 0 && task >= 0 && task < c.a.q_cap) {
+  if (c.a.trace && c.a.trace_tasks && threadIdx.x == 0 && task >= 0 && task < c.a.q_cap) {
     int* p = c.a.trace + 4 * (size_t)task;
     p[0] = c.wg;
     p[1] = (int)t0;
@@ -551,8 +552,10 @@ __device__ __forceinline__ void trace_task(const Ctx& c, int task, long long t0)
   }
 }
 __device__ __forceinline__ void trace_wg(const Ctx& c, int which) {
-  if (c.a.trace && threadIdx.x == 0 && c.wg < 1024)
+  if (c.a.trace && threadIdx.x == 0 && c.wg < 1024) {
     c.a.trace[4 * (size_t)c.a.q_cap + 2 * c.wg + which] = (int)now_ticks();
+    c.a.trace[4 * (size_t)c.a.q_cap + 2048 + 2 * c.wg + which] = (int)__builtin_amdgcn_s_memtime();
+  }
 }
 
 // Prologue: pick this call's bank and re-arm the part of the other bank the

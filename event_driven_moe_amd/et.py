@@ -20,7 +20,7 @@ SCHED_STATIC, SCHED_DYNAMIC, SCHED_BARRIER, SCHED_PER_OP = 0, 1, 2, 3
 SCHEDS = {"static": 0, "dynamic": 1, "barrier": 2, "per_op": 3}
 OK, EINVAL, EWORKSPACE, EHIP, ETIMEOUT, EUNSUPPORTED, ESTATE, ERANGE = range(8)
 WL_SPLITK, WL_MLP, WL_MOE, WL_BLOCK, WL_DECODE = 1, 2, 3, 4, 5
-DEBUG_COUNTS, DEBUG_TRACE, SCRATCH_RESET, DEBUG_WATCHDOG_TICK = 1, 2, 4, 8
+DEBUG_COUNTS, DEBUG_TRACE, SCRATCH_RESET, DEBUG_WATCHDOG_TICK, DEBUG_CLOCK = 1, 2, 4, 8, 16
 
 c_int, c_size_t, c_void_p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 
@@ -92,7 +92,7 @@ def lib():
         L.et_moe_layer_noalloc.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                                            c_void_p, c_void_p, c_void_p, c_void_p, c_int,
                                            P(Opts), c_void_p]
-        L.et_ceiling_mfma.argtypes = [c_void_p, c_int, c_void_p]
+        L.et_ceiling_mfma.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_void_p]
         L.et_ceiling_stream.argtypes = [c_void_p, c_size_t, c_void_p, c_int, c_void_p]
         L.et_read_status.argtypes = [c_void_p, P(Plan), c_void_p, P(Report)]
         L.et_status_str.argtypes = [c_int]
@@ -220,8 +220,18 @@ class Workspace:
         start, end) in 100 MHz ticks (low 32 bits), from ET_DEBUG_TRACE calls."""
         lay = self.layout()
         n = self.plan.max_tasks
-        t = self.view(lay.trace, torch.int32, 4 * n + 2048)
-        return t[:4 * n].view(n, 4), t[4 * n:].view(1024, 2)
+        t = self.view(lay.trace, torch.int32, 4 * n + 4096)
+        return t[:4 * n].view(n, 4), t[4 * n:4 * n + 2048].view(1024, 2)
+
+    def clock_stamps(self):
+        """Workgroups [1024, 2, 2]: (start, end) x (100 MHz real-time counter,
+        shader clock counter), low 32 bits, from ET_DEBUG_TRACE or
+        ET_DEBUG_CLOCK calls."""
+        lay = self.layout()
+        n = self.plan.max_tasks
+        t = self.view(lay.trace, torch.int32, 4 * n + 4096)
+        return torch.stack([t[4 * n:4 * n + 2048].view(1024, 2),
+                            t[4 * n + 2048:].view(1024, 2)], dim=2)
 
 
 def splitk_reduce(A, Bpart, C, ws, sched="static", stream=None, **opts):
@@ -374,9 +384,20 @@ def moe_aux(ws, T, intermediates=False):
     return aux
 
 
-def ceiling_mfma(out, iters, stream=None):
-    """Enqueues the MFMA-only microbenchmark (out: float32 [G*4] device tensor)."""
-    _check(lib().et_ceiling_mfma(_ptr(out, torch.float32, "out"), iters, _stream(stream)),
+def ceiling_mfma(out, iters, operands=None, stamps=None, stream=None):
+    """Enqueues the MFMA-only microbenchmark (out: float32 [G*4] device tensor;
+    operands: None or a bf16 device tensor of G*256*16 elements, the
+    fragments each lane loads; stamps: None or an int64 [G*4] device tensor
+    that receives shader-clock / real-time stamps around the loop)."""
+    if operands is not None and (operands.dtype != torch.bfloat16 or not operands.is_cuda
+                                 or not operands.is_contiguous()
+                                 or operands.numel() < num_workers() * 256 * 16):
+        raise ValueError("operands must be a contiguous bf16 device tensor of G*256*16 elements")
+    if stamps is not None and stamps.numel() < num_workers() * 4:
+        raise ValueError("stamps must hold G*4 int64 values")
+    ops = c_void_p(operands.data_ptr()) if operands is not None else None
+    st = _ptr(stamps, torch.int64, "stamps") if stamps is not None else None
+    _check(lib().et_ceiling_mfma(ops, _ptr(out, torch.float32, "out"), st, iters, _stream(stream)),
            "et_ceiling_mfma")
 
 

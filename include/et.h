@@ -79,9 +79,11 @@ enum {
   ET_DEBUG_TRACE = 2,   /* record each task's workgroup and start / end time (et_layout.trace) */
   ET_SCRATCH_RESET = 4, /* et_moe_layer_noalloc only: clear the library-held scratch state (event
                            counters, ready queue, sticky fault word) before this call */
-  ET_DEBUG_WATCHDOG_TICK = 8  /* watchdog of one 10 ns clock tick instead of timeout_ms: a wait
+  ET_DEBUG_WATCHDOG_TICK = 8, /* watchdog of one 10 ns clock tick instead of timeout_ms: a wait
                                  that is still pending at its first watchdog check ends the call
                                  with ET_ETIMEOUT (tests of the timeout path) */
+  ET_DEBUG_CLOCK = 16   /* record only each workgroup's start / end stamps (et_layout.trace's
+                           workgroup part): the clock a call ran at, without per-task records */
 };
 
 /* Launch modes of the persistent kernels.  Every workgroup of a persistent
@@ -123,7 +125,9 @@ typedef struct et_plan {
   size_t off_slots;    /* ready queue: int32 [8][64] shard control words (claim and push
                           counters), then int32 [8][max_tasks] slots, one array per shard */
   size_t off_runs;     /* int32 [max_tasks] per-task run counts (ET_DEBUG_COUNTS) */
-  size_t off_trace;    /* int32 [max_tasks][4] task trace + [1024][2] workgroup times (ET_DEBUG_TRACE) */
+  size_t off_trace;    /* int32 [max_tasks][4] task trace + [1024][2] workgroup start / end times
+                          (100 MHz real-time counter) + [1024][2] the shader clock counter at the
+                          same points (low 32 bits each; ET_DEBUG_TRACE, ET_DEBUG_CLOCK) */
   size_t off_aux;      /* workload intermediates (see et_layout) */
   size_t aux_bytes;
   int mlp_inter;       /* ET_WL_BLOCK: intermediate size of the dense MLP (else 0) */
@@ -316,14 +320,21 @@ int et_moe_layer_noalloc(const float* logits, const uint16_t* x, int n_tokens, i
  * et_ceiling_mfma: one workgroup of four waves per compute unit, each wave issuing
  *   `iters` blocks of 32 bf16 MFMAs (v_mfma_f32_16x16x32_bf16, 16384 flops each; 8
  *   independent accumulator chains) on register operands, no memory traffic:
- *   flops = G * 4 * iters * 32 * 16384 for G = et_num_workers().  out: float [G * 4] (one value per wave, keeps the
- *   results live).  Timing the launch gives the sustained bf16 MFMA rate.
+ *   flops = G * 4 * iters * 32 * 16384 for G = et_num_workers().  operands: NULL
+ *   (small constants in every lane) or a device buffer (16-byte aligned) of
+ *   G * 256 * 32 bytes -- thread t of workgroup w loads its A and B fragments
+ *   (16 bytes each) from bytes 32 (256 w + t) .. +32 once.  out: float [G * 4] (one
+ *   value per wave, keeps the results live).  stamps: NULL or long long [G * 4] --
+ *   per workgroup the shader clock counter and the 100 MHz real-time counter before
+ *   and after the loop (clock = shader-counter delta / real-time delta x 100 MHz).
+ *   Timing the launch gives the sustained bf16 MFMA rate.
  * et_ceiling_stream: reads `bytes` (a multiple of 16; src 16-byte aligned) with
  *   16-byte loads in a grid-stride loop, G * wgs_per_cu workgroups (1..16 per
  *   compute unit).  out: int [G * wgs_per_cu * 4].  Timing it on a buffer far larger
  *   than the caches gives the sustained HBM read rate.
  * Both enqueue one kernel on `stream` and return ET_OK, ET_EINVAL or ET_EHIP. */
-int et_ceiling_mfma(float* out, int iters, hipStream_t stream);
+int et_ceiling_mfma(const void* operands, float* out, long long* stamps, int iters,
+                    hipStream_t stream);
 int et_ceiling_stream(const void* src, size_t bytes, int* out, int wgs_per_cu,
                       hipStream_t stream);
 

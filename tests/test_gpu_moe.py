@@ -394,3 +394,24 @@ def test_watchdog_timeout_is_reported(sched):
     ws.init()
     _, _, _, _, out2, aux, _ = run_moe("moe_skewed", 1024, sched, ws=ws)
     check_against_oracle("moe_skewed", 1024, out2, aux)
+
+
+@pytest.mark.parametrize("sched", ["static", "dynamic"])
+def test_clock_stamps(sched):
+    """ET_DEBUG_CLOCK records every workgroup's start / end stamps (real time
+    and shader clock) and no per-task records; the output is unchanged, and
+    the clock the stamps give lies in the device's range."""
+    name, T = "moe_skewed", 256
+    ws = _ws(name, 1024)
+    tr, _ = ws.trace()
+    tr.zero_()
+    cfg, logits, x, (wg, wu, wd), out, aux, _ = run_moe(name, T, sched, ws=ws, debug=et.DEBUG_CLOCK)
+    G = et.num_workers()
+    st = ws.clock_stamps()[:G].cpu().long()
+    d_rt = (st[:, 1, 0] - st[:, 0, 0]) & 0xFFFFFFFF
+    d_sc = (st[:, 1, 1] - st[:, 0, 1]) & 0xFFFFFFFF
+    assert (d_rt > 0).all() and (d_sc > 0).all()
+    ghz = float(d_sc.sum()) / float(d_rt.sum()) * 0.1
+    assert 0.3 < ghz < 3.0, ghz
+    assert int(tr.abs().sum()) == 0                     # no per-task records
+    check_against_oracle(name, T, out, aux)
