@@ -86,12 +86,15 @@ __device__ __forceinline__ void norm_rope(float& x0, float& x1, const uint16_t* 
   x1 = y1 * cs + y0 * sn;
 }
 
+// GM: the largest group G = Hq / Hk the instance handles (8 or 16); the
+// value accumulators of a lane take 8 * GM registers.
+template <int GM>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeArgs a) {
   __shared__ Shared sh;
-  __shared__ __align__(16) float qs[kMaxGroup][kHeadDim];
-  __shared__ __align__(16) float sc[kMaxGroup][kAttnChunk];
-  __shared__ __align__(16) float part[4][kMaxGroup][kHeadDim];
-  __shared__ float m_run[kMaxGroup], l_run[kMaxGroup], alpha[kMaxGroup];
+  __shared__ __align__(16) float qs[GM][kHeadDim];
+  __shared__ __align__(16) float sc[GM][kAttnChunk];
+  __shared__ __align__(16) float part[4][GM][kHeadDim];
+  __shared__ float m_run[GM], l_run[GM], alpha[GM];
 
   Ctx c;
   if (!prologue(c, ra, &sh)) return;
@@ -182,21 +185,26 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
     const size_t rstride = (size_t)a.Hk * kHeadDim;                 // elements between positions
     const size_t base = ((size_t)b * a.S * a.Hk + h) * kHeadDim;    // position 0 of this head
     const Rsrc rk = make_rsrc(a.kc + base, (uint32_t)((size_t)n * rstride * 2));
-    const int dp = lane;          // value columns 2 dp, 2 dp + 1
-    float o[kMaxGroup][2];
+    // value rows: lane (rq = lane / 16, cc = lane % 16) accumulates columns
+    // 8 cc .. 8 cc + 7 of the rows 4 r + rq its wave takes
+    const int rq = lane >> 4, cc = lane & 15;
+    float o[GM][8];
 #pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g) o[g][0] = o[g][1] = 0.f;
+    for (int g = 0; g < GM; ++g)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[g][j] = 0.f;
     // The newest position (n - 1) was written in this launch and is read
-    // with coherent loads; the others are inputs.  Loads are issued in
-    // batches before their values are used (a load per use put a full
-    // memory latency on every position).
+    // with coherent loads; the others are inputs.  A chunk's key rows are
+    // requested before the previous chunk's value rows are used, and each
+    // wave requests its value rows of a chunk in one or two batches of
+    // 16-byte loads (a 4-byte load per lane per row, 16 rows in flight per
+    // wave, put about five memory latencies on every chunk).
     const int qlast = n - 1;
     const Rsrc rv = make_rsrc(a.vc + base, (uint32_t)((size_t)n * rstride * 2));
-    for (int c0 = p0; c0 < p1; c0 += kAttnChunk) {
-      // scores of position c0 + tid for every head of the group
+    i32x4 kr[kHeadDim / 8];
+    auto load_keys = [&](int c0) ET_INLINE {
       const int pp = c0 + tid;
       const uint32_t off = pp < p1 ? (uint32_t)(pp * rstride * 2) : kOOB;
-      i32x4 kr[kHeadDim / 8];
       if (pp == qlast) {
 #pragma unroll
         for (int j = 0; j < kHeadDim / 8; ++j) kr[j] = ld16c(rk, off + 16u * j);
@@ -204,9 +212,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
 #pragma unroll
         for (int j = 0; j < kHeadDim / 8; ++j) kr[j] = ld16(rk, off + 16u * j);
       }
-      float s[kMaxGroup];
+    };
+    constexpr int kVB = GM <= 8 ? 16 : 8;      // value loads per batch per lane
+    if (p0 < p1) load_keys(p0);
+    for (int c0 = p0; c0 < p1; c0 += kAttnChunk) {
+      // scores of position c0 + tid for every head of the group
+      const int pp = c0 + tid;
+      float s[GM];
 #pragma unroll
-      for (int g = 0; g < kMaxGroup; ++g) s[g] = 0.f;
+      for (int g = 0; g < GM; ++g) s[g] = 0.f;
 #pragma unroll
       for (int j = 0; j < kHeadDim / 8; ++j) {
         float kf[8];
@@ -216,7 +230,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
           kf[2 * t + 1] = __builtin_bit_cast(float, (uint32_t)kr[j][t] & 0xffff0000u);
         }
 #pragma unroll
-        for (int g = 0; g < kMaxGroup; ++g)
+        for (int g = 0; g < GM; ++g)
           if (g < G) {
             const float4 qa = *reinterpret_cast<const float4*>(&qs[g][8 * j]);
             const float4 qb = *reinterpret_cast<const float4*>(&qs[g][8 * j + 4]);
@@ -247,50 +261,59 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(RunArgs ra, DecodeA
         }
       }
       __syncthreads();
-      // value rows: wave w takes positions c0 + w, c0 + w + 4, ...; lane dp
-      // columns 2 dp, 2 dp + 1 of every head; 16 rows requested per batch
 #pragma unroll
-      for (int g = 0; g < kMaxGroup; ++g)
+      for (int g = 0; g < GM; ++g)
         if (g < G) {
-          o[g][0] *= alpha[g];
-          o[g][1] *= alpha[g];
+          const float al = alpha[g];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o[g][j] *= al;
         }
+      // rows past the split's end load nothing and carry probability 0
       const int cend = min(p1, c0 + kAttnChunk);
-      const int vend = min(cend, qlast);       // input rows (plain loads)
-      auto add_row = [&](int q, uint32_t two) ET_INLINE {
-        const float v0 = __builtin_bit_cast(float, two << 16);
-        const float v1 = __builtin_bit_cast(float, two & 0xffff0000u);
+      const bool coh = qlast >= c0 && qlast < cend;
 #pragma unroll
-        for (int g = 0; g < kMaxGroup; ++g)
-          if (g < G) {
-            const float e = sc[g][q - c0];
-            o[g][0] += e * v0;
-            o[g][1] += e * v1;
-          }
-      };
-      for (int q0 = c0 + wave; q0 < vend; q0 += 4 * 16) {
-        uint32_t vv[16];
+      for (int t0 = 0; t0 < 16; t0 += kVB) {
+        i32x4 vv[kVB];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int q = q0 + 4 * t;
-          vv[t] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
-              rv, q < vend ? (int)((q * rstride + 2 * dp) * 2) : (int)kOOB, 0, 0);
+        for (int t = 0; t < kVB; ++t) {
+          const int q = c0 + 16 * (t0 + t) + 4 * wave + rq;
+          const uint32_t off = q < cend ? (uint32_t)((q * rstride + 8 * cc) * 2) : kOOB;
+          vv[t] = coh ? ld16c(rv, off) : ld16(rv, off);
         }
+        // the next chunk's key rows, behind this chunk's value rows
+        if (t0 + kVB == 16 && c0 + kAttnChunk < p1) load_keys(c0 + kAttnChunk);
 #pragma unroll
-        for (int t = 0; t < 16; ++t)
-          if (q0 + 4 * t < vend) add_row(q0 + 4 * t, vv[t]);
+        for (int t = 0; t < kVB; ++t) {
+          const int r = 16 * (t0 + t) + 4 * wave + rq;    // row within the chunk
+          float vf[8];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            vf[2 * u] = __builtin_bit_cast(float, (uint32_t)vv[t][u] << 16);
+            vf[2 * u + 1] = __builtin_bit_cast(float, (uint32_t)vv[t][u] & 0xffff0000u);
+          }
+#pragma unroll
+          for (int g = 0; g < GM; ++g)
+            if (g < G) {
+              const float e = sc[g][r];
+#pragma unroll
+              for (int j = 0; j < 8; ++j) o[g][j] += e * vf[j];
+            }
+        }
       }
-      if (qlast >= c0 && qlast < cend && ((qlast - c0) & 3) == wave)
-        add_row(qlast, (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
-                           rv, (int)((qlast * rstride + 2 * dp) * 2), 0, 16));
       __syncthreads();
     }
-    // the four waves' partial sums, then the softmax denominator
+    // the four row groups of a wave (lanes 16 apart), then the four waves'
+    // partial sums, then the softmax denominator
 #pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g)
+    for (int g = 0; g < GM; ++g)
       if (g < G) {
-        part[wave][g][2 * dp] = o[g][0];
-        part[wave][g][2 * dp + 1] = o[g][1];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float v = o[g][j];
+          v += __shfl_xor(v, 16);
+          v += __shfl_xor(v, 32);
+          if (rq == 0) part[wave][g][8 * cc + j] = v;
+        }
       }
     __syncthreads();
     const size_t ps = (size_t)i * a.NS + split;          // this split's partial
@@ -440,7 +463,8 @@ int launch_decode(const LaunchCommon& lc, const uint16_t* q, const uint16_t* k,
   ra.n_init = 2 * N - ra.init_base;              // the rest are implicit queue entries
   ra.total_hint = 2 * N + N * a.NS + N - ra.init_base;   // queue tasks: those and the pushed ones
   ra.extent = EV_DEC_FIXED + 2 * N;
-  const void* kern = reinterpret_cast<const void*>(&decode_kernel);
+  const void* kern = a.G <= 8 ? reinterpret_cast<const void*>(&decode_kernel<8>)
+                              : reinterpret_cast<const void*>(&decode_kernel<16>);
   if (lc.sched == ET_SCHED_PER_OP) {
     for (int ph = 0; ph < 4; ++ph) {
       ra.phase = ph;
