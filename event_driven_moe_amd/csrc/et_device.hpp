@@ -143,7 +143,7 @@ __device__ __forceinline__ int spin_until(const Ctx& c, int idx, int wait_count,
     __builtin_amdgcn_s_sleep(1);
     v = ld_rlx(p);
     if (v == target) return 1;
-    if ((it & 63) == 0) {
+    if ((it & 63) == 0 || c.a.timeout <= 1) {   // one-tick watchdog: check every poll
       if (faulted(c.a)) return 0;
       if (now_ticks() - t0 > c.a.timeout) {
         raise_fault(c.a, ET_ETIMEOUT, task, idx, v);
@@ -179,7 +179,7 @@ __device__ __forceinline__ int spin_until_all(const Ctx& c, int first, int n, in
       if (__ballot(v < target) != 0) return 0;
       if (it == 0) t0 = now_ticks();
       __builtin_amdgcn_s_sleep(1);
-      if ((it & 63) == 63) {
+      if ((it & 63) == 63 || c.a.timeout <= 1) {
         if (faulted(c.a)) return 0;
         if (now_ticks() - t0 > c.a.timeout) {
           if (lane == 0) raise_fault(c.a, ET_ETIMEOUT, task, first + base, n);
@@ -305,7 +305,7 @@ __device__ __forceinline__ int spin_flag(const Ctx& c, int idx, int slot, int ta
   for (int it = 1;; ++it) {
     __builtin_amdgcn_s_sleep(1);
     if (ld_rlx(p) == c.gen) return 1;
-    if ((it & 63) == 0) {
+    if ((it & 63) == 0 || c.a.timeout <= 1) {   // one-tick watchdog: check every poll
       if (faulted(c.a)) return 0;
       if (now_ticks() - t0 > c.a.timeout) {
         raise_fault(c.a, ET_ETIMEOUT, task, idx, ld_rlx(c.ev + idx));
@@ -447,7 +447,7 @@ __device__ __forceinline__ int resolve_slot(const Ctx& c, int q, int idx) {
     }
     if (it == 0) t0 = now_ticks();
     __builtin_amdgcn_s_sleep(1);
-    if ((it & 63) == 63) {
+    if ((it & 63) == 63 || a.timeout <= 1) {
       if (faulted(a)) return -2;
       if (now_ticks() - t0 > a.timeout) {
         raise_fault(a, ET_ETIMEOUT, -1, idx, q);

@@ -328,11 +328,13 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     const int nq = ncols / 8;              // 8 columns (16 bytes of bf16) per item
     const int nit = ntok * nq;
     // IT items per thread per pass, all KM * IT row loads issued before any
-    // sum (IT = 2 when k <= 8 keeps the loads within 64 registers)
+    // sum (IT = 2 when k <= 8 keeps the loads within 64 registers); with
+    // several passes (wide tiles) the next pass's rows are requested before
+    // the current pass is summed, so the tile pays about one memory round
+    // trip, not one per pass
     auto pass = [&](auto km_c, auto it_c) ET_INLINE {
       constexpr int KM = decltype(km_c)::value, IT = decltype(it_c)::value;
-      for (int i0 = tid; i0 < nit; i0 += IT * kThreads) {
-        i32x4 yv[IT][KM];
+      auto issue = [&](int i0, i32x4 (&yv)[IT][KM]) ET_INLINE {
 #pragma unroll
         for (int u = 0; u < IT; ++u) {
           const int i = i0 + u * kThreads;
@@ -341,6 +343,8 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
           for (int s = 0; s < KM; ++s)
             if (s < k && i < nit) yv[u][s] = ld16c(ry, (uint32_t)((cp[ti * k + s] * (size_t)m.H + col) * 2));
         }
+      };
+      auto finish = [&](int i0, const i32x4 (&yv)[IT][KM]) ET_INLINE {
 #pragma unroll
         for (int u = 0; u < IT; ++u) {
           const int i = i0 + u * kThreads;
@@ -373,6 +377,16 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
                   (uint32_t)((size_t)tok_of(ti) * m.H + col) * 2u, zv);
           }
         }
+      };
+      constexpr int kStep = IT * kThreads;
+      i32x4 ya[IT][KM], yb[IT][KM];
+      if (tid < nit) issue(tid, ya);
+      for (int i0 = tid; i0 < nit; i0 += 2 * kStep) {
+        if (i0 + kStep < nit) issue(i0 + kStep, yb);
+        finish(i0, ya);
+        if (i0 + kStep >= nit) break;
+        if (i0 + 2 * kStep < nit) issue(i0 + 2 * kStep, ya);
+        finish(i0 + kStep, yb);
       }
     };
     using std::integral_constant;
@@ -1418,7 +1432,9 @@ inline int moe_setup(const LaunchCommon& lc, const MoePlan& mp, const MoeAux& ax
   m.tpr = mp.tpr(T);
   // combine tiles: 16 tokens x 256 columns, or x 64 columns when that leaves
   // workgroups without a tile
-  m.ccols = cdiv(T, kCombTok) * cdiv(m.H, kCombCols) >= lc.G ? kCombCols : kCombColsMin;
+  m.ccols = cdiv(T, kCombTok) * cdiv(m.H, kCombColsWide) >= 4 * lc.G ? kCombColsWide
+            : cdiv(T, kCombTok) * cdiv(m.H, kCombCols) >= lc.G       ? kCombCols
+                                                                       : kCombColsMin;
   m.ev_exp = mp.ev_exp();
   m.ev_he = mp.ev_he();
   m.ev_h = mp.ev_h();

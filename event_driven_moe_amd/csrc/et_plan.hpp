@@ -142,6 +142,7 @@ struct MlpPlan {
 constexpr int kCombTok = 16;
 constexpr int kCombCols = 256;      // combine tile columns (64 when 256 gives fewer tiles than CUs)
 constexpr int kCombColsMin = 64;
+constexpr int kCombColsWide = 1024; // ... and 1024 when that still gives 4 tiles per CU
 constexpr int kCombGroupRounds = 4;   // static: E_cg when down tiles <= this many per workgroup
 constexpr int kCombGroupMin = 16;     //   and at least this many token groups
 constexpr int kMaxExperts = 1024;

@@ -79,9 +79,9 @@ enum {
   ET_DEBUG_TRACE = 2,   /* record each task's workgroup and start / end time (et_layout.trace) */
   ET_SCRATCH_RESET = 4, /* et_moe_layer_noalloc only: clear the library-held scratch state (event
                            counters, ready queue, sticky fault word) before this call */
-  ET_DEBUG_WATCHDOG_TICK = 8, /* watchdog of one 10 ns clock tick instead of timeout_ms: a wait
-                                 that is still pending at its first watchdog check ends the call
-                                 with ET_ETIMEOUT (tests of the timeout path) */
+  ET_DEBUG_WATCHDOG_TICK = 8, /* watchdog of one 10 ns clock tick instead of timeout_ms, checked
+                                 at every poll: a wait that is not satisfied at its first poll
+                                 ends the call with ET_ETIMEOUT (tests of the timeout path) */
   ET_DEBUG_CLOCK = 16   /* record only each workgroup's start / end stamps (et_layout.trace's
                            workgroup part): the clock a call ran at, without per-task records */
 };

@@ -375,8 +375,8 @@ def test_central_queue(T):
 
 @pytest.mark.parametrize("sched", ["static", "dynamic", "barrier"])
 def test_watchdog_timeout_is_reported(sched):
-    """A one-tick watchdog (forced from the host) makes the first wait still
-    pending at its check end the call: the device records ET_ETIMEOUT, every
+    """A one-tick watchdog (forced from the host, checked at every poll) makes
+    the first wait not satisfied at its first poll end the call: the device records ET_ETIMEOUT, every
     workgroup leaves (the call completes), later calls do nothing until the
     workspace is re-initialised, and then the layer matches the oracle again."""
     ws = et.Workspace(et.WL_MOE, 1024, 2048, 768, 128, 8, device=DEV)
