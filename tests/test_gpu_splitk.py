@@ -117,3 +117,21 @@ def test_central_queue(ws):
     B8, C8 = _run(ws, A, "dynamic")
     B1, C1 = _run(ws, A, "dynamic", queue_shards=1)
     assert np.array_equal(C8, C1) and np.array_equal(B8, B1)
+
+
+def test_init_leaves_queue_total_unknown(ws):
+    """et_workspace_init writes every header word exactly once: the ready
+    queue's task total (header word 160) reads "unknown" (INT32_MAX) after
+    init, so the first dynamic call's workers wait for pushed slots instead
+    of giving up claimed ones (a stray zero there would leave stage-2 rows
+    unwritten).  Init, check the word, then a dynamic call against the
+    oracle, several times over."""
+    A = synth.splitk_inputs(rows=2048, seed=121, device=DEV, integer=True)
+    Bref, Cref = osk.splitk_reduce(A.cpu().numpy())
+    for _ in range(8):
+        ws.init()
+        torch.cuda.synchronize()
+        hdr = ws.view(0, torch.int32, 256).cpu()
+        assert int(hdr[160]) == 0x7FFFFFFF
+        B, C = _run(ws, A, "dynamic")
+        assert np.array_equal(B, Bref) and np.array_equal(C, Cref)
