@@ -327,29 +327,43 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     __syncthreads();
     const int nq = ncols / 8;              // 8 columns (16 bytes of bf16) per item
     const int nit = ntok * nq;
+    const Rsrc rout = make_rsrc(m.out, (uint32_t)((size_t)m.T * m.H * 4));
     // IT items per thread per pass, all KM * IT row loads issued before any
-    // sum (IT = 2 when k <= 8 keeps the loads within 64 registers); with
-    // several passes (wide tiles) the next pass's rows are requested before
-    // the current pass is summed, so the tile pays about one memory round
-    // trip, not one per pass
+    // sum (IT = 2 when k <= 8 keeps the loads within 64 registers); the next
+    // pass's rows are requested before the current pass is summed, so the
+    // tile pays about one memory round trip, not one per pass.  No memory
+    // access sits in a branch: items past the tile and slots past k load and
+    // store at an out-of-range offset (the hardware drops those), and the
+    // pass loop issues one pass past the last.  With a load or store under a
+    // branch the compiler can no longer count which loads are still in
+    // flight at each wait, and it waited for all but the last two before
+    // every load, serialising the pass.
     auto pass = [&](auto km_c, auto it_c) ET_INLINE {
       constexpr int KM = decltype(km_c)::value, IT = decltype(it_c)::value;
       auto issue = [&](int i0, i32x4 (&yv)[IT][KM]) ET_INLINE {
+        uint32_t off[IT][KM];
 #pragma unroll
         for (int u = 0; u < IT; ++u) {
           const int i = i0 + u * kThreads;
-          const int ti = i / nq, col = c0 + 8 * (i % nq);
+          const bool ok = i < nit;
+          const int ti = ok ? i / nq : 0, col = c0 + 8 * (i % nq);
 #pragma unroll
-          for (int s = 0; s < KM; ++s)
-            if (s < k && i < nit) yv[u][s] = ld16c(ry, (uint32_t)((cp[ti * k + s] * (size_t)m.H + col) * 2));
+          for (int s = 0; s < KM; ++s) {
+            const int pos = cp[ti * k + (s < k ? s : 0)];
+            off[u][s] = ok && s < k ? (uint32_t)((pos * (size_t)m.H + col) * 2) : kOOB;
+          }
         }
+#pragma unroll
+        for (int u = 0; u < IT; ++u)
+#pragma unroll
+          for (int s = 0; s < KM; ++s) yv[u][s] = ld16c(ry, off[u][s]);
       };
       auto finish = [&](int i0, const i32x4 (&yv)[IT][KM]) ET_INLINE {
 #pragma unroll
         for (int u = 0; u < IT; ++u) {
           const int i = i0 + u * kThreads;
-          if (i >= nit) break;
-          const int ti = i / nq, col = c0 + 8 * (i % nq);
+          const bool ok = i < nit;
+          const int ti = ok ? i / nq : 0, col = c0 + 8 * (i % nq);
           float acc[8];
 #pragma unroll
           for (int q = 0; q < 8; ++q) acc[q] = 0.f;
@@ -364,29 +378,34 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
                 acc[2 * q + 1] = __fmaf_rn(w, __builtin_bit_cast(float, two & 0xffff0000u), acc[2 * q + 1]);
               }
             }
-          float4* o = reinterpret_cast<float4*>(m.out + (size_t)tok_of(ti) * m.H + col);
-          o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-          o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+          const size_t el = (size_t)tok_of(ti) * m.H + col;
+          const uint32_t oo = ok ? (uint32_t)(el * 4) : kOOB;
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(i32x4, make_float4(acc[0], acc[1], acc[2], acc[3])), rout, (int)oo, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(i32x4, make_float4(acc[4], acc[5], acc[6], acc[7])), rout,
+              (int)(ok ? oo + 16u : kOOB), 0, 0);
           if constexpr (kBlock) {
             // the dense MLP's input: the same rows rounded to bf16
             i32x4 zv;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               zv[q] = (int)((uint32_t)f32_to_bf16(acc[2 * q]) | ((uint32_t)f32_to_bf16(acc[2 * q + 1]) << 16));
-            st16c(make_rsrc(m.zb, (uint32_t)m.T * m.H * 2),
-                  (uint32_t)((size_t)tok_of(ti) * m.H + col) * 2u, zv);
+            st16c(make_rsrc(m.zb, (uint32_t)m.T * m.H * 2), ok ? (uint32_t)(el * 2) : kOOB, zv);
           }
         }
       };
       constexpr int kStep = IT * kThreads;
+      const int npass = cdiv(nit, kStep);   // the same in every thread
       i32x4 ya[IT][KM], yb[IT][KM];
-      if (tid < nit) issue(tid, ya);
-      for (int i0 = tid; i0 < nit; i0 += 2 * kStep) {
-        if (i0 + kStep < nit) issue(i0 + kStep, yb);
-        finish(i0, ya);
-        if (i0 + kStep >= nit) break;
-        if (i0 + 2 * kStep < nit) issue(i0 + 2 * kStep, ya);
-        finish(i0 + kStep, yb);
+      issue(tid, ya);
+      for (int p = 0;; p += 2) {
+        issue(tid + (p + 1) * kStep, yb);
+        finish(tid + p * kStep, ya);
+        if (p + 1 >= npass) break;
+        issue(tid + (p + 2) * kStep, ya);
+        finish(tid + (p + 1) * kStep, yb);
+        if (p + 2 >= npass) break;
       }
     };
     using std::integral_constant;

@@ -10,7 +10,7 @@ block is checked, the last row of each block first, so every expert's
 partial last block is among them; since whole output rows are compared,
 every gate/up and down column tile of each block is covered.  At T = 512
 every token is compared.  The fp64 oracle evaluates each expert once per T
-and the result serves both schedules."""
+and the result serves every schedule."""
 
 import numpy as np
 import pytest
@@ -78,7 +78,7 @@ def reference(T):
 
 
 @pytest.mark.parametrize("T", [512, 2048, 8192])
-@pytest.mark.parametrize("sched", ["static", "dynamic"])
+@pytest.mark.parametrize("sched", ["static", "dynamic", "barrier", "per_op"])
 def test_full_size_block_cover(ws, T, sched):
     cfg = synth.MOE_PRESETS[NAME]
     wg, wu, wd = moe_weights(NAME)
