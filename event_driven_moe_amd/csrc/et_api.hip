@@ -89,6 +89,8 @@ int fill_common(LaunchCommon& lc, void* ws, const et_plan* plan, int sched, cons
   if (lc.coop != ET_LAUNCH_ORDINARY && lc.coop != ET_LAUNCH_COOPERATIVE) return ET_EINVAL;
   lc.shards = o && o->queue_shards ? o->queue_shards : kMaxShards;
   if (lc.shards != 1 && lc.shards != kMaxShards) return ET_EINVAL;
+  lc.qorder = o ? o->queue_order : ET_QORDER_AUTO;
+  if (lc.qorder < ET_QORDER_AUTO || lc.qorder > ET_QORDER_STATIC) return ET_EINVAL;
   lc.stream = stream;
   return workers_for_current_device(&lc.G);
 }

@@ -20,6 +20,7 @@ struct LaunchCommon {
   int tile;
   int coop;            // persistent launches: cooperative (1) or ordinary (0)
   int shards;          // dynamic mode: ready-queue shards (1 or kMaxShards)
+  int qorder;          // dynamic mode, MoE: ET_QORDER_*
   int G;               // workgroups of a persistent launch (one per CU)
   hipStream_t stream;
 

@@ -78,6 +78,7 @@ struct MoeArgs {
   float* y2;           // [T, H] dense MLP output
   int Im;
   int ev_z, ev_hm;     // E_z[mb] (combine tiles of row block mb), E_hm[mb][Im / 128]
+  int qall;   // dynamic: every GEMM task queued at the scan in static order (ET_QORDER_STATIC)
 };
 
 // LDS: three slot arrays (the GEMM ring of the wide variants; scratch for
@@ -98,6 +99,12 @@ constexpr int kInlineCombineTokens = 4;
 // Dynamic schedule: with at most this many gate/up tasks per workgroup, routing
 // chunk 0 alone pushes them (early push); with more, every chunk pushes a share.
 constexpr int kSoloPush = 4;
+// Dynamic schedule, ET_QORDER_AUTO: the static-order queue from this many
+// GEMM tasks per worker on (moe_large T = 2048 / 8192 dynamic: 4.03 / 8.06 ms
+// with tasks pushed as they become ready, 3.83 / 7.68 ms in static order with
+// one-slot claims; moe_skewed T = 1024, 5 tasks per worker: 220 us against
+// 233 us, where the ready order wins).
+constexpr int kQAllTasks = 16;
 constexpr int kIdxCache = 2 * (kMaxExperts + 1) * 4;   // tok_indptr + blk_indptr copies
 constexpr int kGenBytes = kGenIdx + kIdxCache;
 
@@ -910,7 +917,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     wg_release();
     if (sched == ET_SCHED_BARRIER) {
       t0_notify_bcast(c, EV_G1ALL, EV_G1ALL, 1, meta(MD_TOTAL1), task);
-    } else if (sched == ET_SCHED_STATIC) {
+    } else if (sched == ET_SCHED_STATIC || m.qall) {
       t0_notify(c, m.ev_h + gb, 1, nt1, task);
     } else {
       // dynamic: the expert's event counts its gate/up tiles over all of its
@@ -954,7 +961,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     const Rsrc rh = make_rsrc(m.h, (uint32_t)m.T * m.k * m.I * 2);
     auto gate = [&](int round) ET_INLINE -> bool {
       if (round != 0) return true;
-      if (sched == ET_SCHED_STATIC) {
+      if (sched == ET_SCHED_STATIC || m.qall) {
         if (!wg_wait(c, m.ev_h + gb, nt1, task)) return false;
       } else if (sched == ET_SCHED_BARRIER && !seen_g1) {
         if (!wg_wait_bcast(c, EV_G1ALL, EV_G1ALL, task)) return false;
@@ -1260,7 +1267,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
         if (task == 0) set_total(c, nb * (nt1 + nt2) + ncomb + (kBlock ? n_mg + n_md : 0));
         const int total1 = nb * nt1;
         const bool solo_push = total1 <= kSoloPush * c.G;
-        if (!solo_push || task == 0) {
+        if (!m.qall && (!solo_push || task == 0)) {
           wg_release();
           if (task != 0 && many_chunks && !wg_wait_bcast(c, EV_SCAN, EV_SCAN, task)) return false;
           const int* blk = reinterpret_cast<const int*>(s1) + 1024;   // exclusive block offsets
@@ -1311,6 +1318,21 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
           const int old = add_rlx(c.ev + m.ev_exp + e, -n);
           if (old - n < -wcnt) raise_fault(ra, ET_ESTATE, task, m.ev_exp + e, old - n);
         }
+      }
+      if (m.qall && task == 0) {
+        // Static-order queue: chunk 0, its own tokens grouped, pushes every
+        // gate/up task and then every down task in task-id order, position
+        // p = id - base1 to the shard of the XCD the static schedule runs p
+        // on (XCD (p mod G) / (G / 8): G / 8 consecutive positions per XCD
+        // and round), so a shard's consecutive slots are the row blocks
+        // sharing one weight tile.  Every gate/up task precedes every
+        // down task in each shard and a down task waits only on gate/up
+        // tasks, so a worker that waits on a claimed down task never holds
+        // back a task it waits for.
+        wg_release();
+        const int per = c.G / 8;
+        wg_push(c, nb * (nt1 + nt2), [&](int i) { return base1 + i; },
+                [&](int i) { return c.G % 8 == 0 ? (i % c.G) / per : (i % c.G) % 8; });
       }
       return true;
     }
@@ -1458,10 +1480,18 @@ inline int moe_setup(const LaunchCommon& lc, const MoePlan& mp, const MoeAux& ax
   m.ev_he = mp.ev_he();
   m.ev_h = mp.ev_h();
   m.ev_c = mp.ev_c();
+  // static-order queue (dynamic schedule): forced, or for the wide tiles
+  // when the call has at least kQAllTasks GEMM tasks per worker (counting
+  // each expert's rows as full blocks, a lower bound)
+  const bool wide = tv == TV_W64 || tv == TV_W128;
+  const long long est_tasks = (long long)T * m.k / (16 * tl.mt) * (m.I / tl.bn1 + m.H / tl.bn2);
+  m.qall = lc.sched == ET_SCHED_DYNAMIC &&
+           (lc.qorder == ET_QORDER_STATIC ||
+            (lc.qorder == ET_QORDER_AUTO && wide && est_tasks >= (long long)kQAllTasks * lc.G));
   ra = lc.run_args();
   ra.init_base = m.NR;   // dynamic: routing runs on workgroups 0..NR-1
   ra.n_init = 0;         // the queue holds pushed tasks only
-  ra.n_single = 0;
+  ra.n_single = m.qall ? (1 << 30) : 0;   // static order: every claim takes one slot
   ra.total_hint = kUnknownTotal;
   ra.extent = mp.extent(T, tl);
   return ET_OK;

@@ -110,7 +110,27 @@ typedef struct et_opts {
   int queue_shards;  /* dynamic mode: ready-queue shards, 1 (one central queue) or 8 (one per
                         XCD: a pushed task goes to the shard its weight tile hashes to, and a
                         worker pops only the shard of its own XCD); 0 = default (8) */
+  int queue_order;   /* dynamic mode, MoE layer and chain: ET_QORDER_* (default ET_QORDER_AUTO) */
 } et_opts;
+
+/* Dynamic schedule of the MoE GEMM tasks (et_opts.queue_order).
+ * READY: the scan pushes every gate/up task early (each waits on its expert's
+ *   grouping event, E_exp); the notify that completes an expert's gate/up
+ *   tiles (E_he) pushes its down tasks, which enter the queue ready to run.
+ * STATIC: once its grouping is done, routing chunk 0 pushes every gate/up and
+ *   down task in the static schedule's order, each to the shard of the XCD
+ *   the static schedule would run it on; down tasks wait on their row block's
+ *   E_h event, and claims take one slot (the consecutive slots of a shard are
+ *   the row blocks sharing a weight tile, which then stream it side by side).
+ *   The early-push form of the dynamic schedule (Event Tensor notes, section
+ *   on dynamic scheduling and its appendix).
+ * AUTO: STATIC for the 128- and 64-row GEMM tiles when the call has at least
+ *   16 GEMM tasks per worker, else READY. */
+enum {
+  ET_QORDER_AUTO = 0,
+  ET_QORDER_READY = 1,
+  ET_QORDER_STATIC = 2
+};
 
 /* Workspace plan: dimensions and byte offsets of every region.  Filled by
  * et_plan_workspace(); passed unchanged to every call on that workspace. */

@@ -98,6 +98,14 @@ def test_block_parity_1024(sched):
     check("moe_skewed", 1024, x, wr, z, y, aux)
 
 
+@pytest.mark.parametrize("name,T", [("moe_small", 8), ("moe_skewed", 1024)])
+def test_block_static_order_queue(name, T):
+    """The chain under the dynamic schedule with the MoE GEMM tasks queued at
+    the scan in the static order."""
+    _, x, wr, z, y, aux = run_block(name, T, "dynamic", queue_order="static")
+    check(name, T, x, wr, z, y, aux)
+
+
 @pytest.mark.parametrize("name,T", [("moe_small", 8), ("moe_skewed", 256)])
 def test_block_schedules_bit_identical(name, T):
     outs = [run_block(name, T, s)[3:5] for s in SCHEDS]

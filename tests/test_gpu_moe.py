@@ -103,6 +103,18 @@ def test_tile_variants(tile, sched, T):
     check_against_oracle("moe_skewed", T, out, aux, tile=tile)
 
 
+@pytest.mark.parametrize("name,T", [("moe_small", 8), ("moe_small", 32), ("moe_skewed", 64),
+                                    ("moe_skewed", 1024), ("moe_skewed_cal", 256)])
+@pytest.mark.parametrize("tile", [-1, 3, 4])
+@pytest.mark.parametrize("fetch", [1, 8])
+def test_static_order_queue(name, T, tile, fetch):
+    """Dynamic schedule with every GEMM task queued at the scan in the static
+    order (claims of one slot whatever the fetch batch), on every tile kind."""
+    _, _, _, _, out, aux, _ = run_moe(name, T, "dynamic", queue_order="static", tile=tile,
+                                      fetch_batch=fetch)
+    check_against_oracle(name, T, out, aux, tile)
+
+
 @pytest.mark.parametrize("fetch", [1, 8])
 def test_fetch_batches(fetch):
     _, _, _, _, out, aux, _ = run_moe("moe_skewed", 256, "dynamic", fetch_batch=fetch)
@@ -110,17 +122,22 @@ def test_fetch_batches(fetch):
 
 
 @pytest.mark.parametrize("T", [16, 64, 256, 1024])
-@pytest.mark.parametrize("sched", ["static", "dynamic"])
+@pytest.mark.parametrize("sched", ["static", "dynamic", "dynamic_static"])
 def test_event_invariants(sched, T):
     """Each task ran once; the data-dependent expert events ended at their
-    run-time wait counts (rows routed to each expert; dynamic: also the
-    gate/up tiles over each expert's blocks), the static schedule's block
-    events at the number of gate/up tiles of a block, and every combine
-    tile's event at its rows times overlapping down tiles."""
+    run-time wait counts (rows routed to each expert; dynamic, tasks pushed
+    as they become ready: also the gate/up tiles over each expert's blocks),
+    the block events (static schedule and the dynamic static-order queue) at
+    the number of gate/up tiles of a block, and every combine tile's event at
+    its rows times overlapping down tiles."""
     name = "moe_skewed"
     ws = _ws(name, 1024)
     ws.runs().zero_()
-    cfg, _, _, _, out, aux, _ = run_moe(name, T, sched, ws=ws, debug=et.DEBUG_COUNTS)
+    qstatic = sched == "dynamic_static"
+    if qstatic:
+        sched = "dynamic"
+    cfg, _, _, _, out, aux, _ = run_moe(name, T, sched, ws=ws, debug=et.DEBUG_COUNTS,
+                                        queue_order="static" if qstatic else "auto")
     st = ws.status()
     E, k, H, I = cfg["n_experts"], cfg["top_k"], cfg["hidden"], cfg["inter"]
     nr = min(128, 8192 // E, -(-T // 8))   # routing chunks of about 8 tokens
@@ -146,7 +163,13 @@ def test_event_invariants(sched, T):
     else:
         assert cnt[4] == -tab["tasks"]["down"]            # all down tiles done
         assert (cnt[ev_c:ev_c + ncg] == 0).all()
-    if sched == "dynamic":
+    if sched == "dynamic" and qstatic:
+        # data-dependent rows per expert; down tiles wait on their block
+        assert (cnt[ev_exp:ev_exp + E] == -tab["events"]["E_exp"]["wait_count"]).all()
+        assert (cnt[ev_h:ev_h + nb] == -tab["events"]["E_h"]["wait_count"]).all()
+        assert (cnt[ev_he:ev_he + E] == 0).all()
+        assert cnt[1] == (-1 if nr >= 16 else 0) and cnt[2] == 0
+    elif sched == "dynamic":
         # data-dependent: rows per expert, and gate/up tiles over its blocks
         assert (cnt[ev_exp:ev_exp + E] == -tab["events"]["E_exp"]["wait_count"]).all()
         assert (cnt[ev_he:ev_he + E] == -tab["events"]["E_he"]["wait_count"]).all()

@@ -77,15 +77,22 @@ def reference(T):
     return _REF[T]
 
 
+# "dynamic" takes the queue order the library picks (tasks pushed as they
+# become ready at T = 512, the static-order queue from T = 2048 on);
+# "dynamic_ready" / "dynamic_static" force one order.
 @pytest.mark.parametrize("T", [512, 2048, 8192])
-@pytest.mark.parametrize("sched", ["static", "dynamic", "barrier", "per_op"])
+@pytest.mark.parametrize("sched", ["static", "dynamic", "barrier", "per_op", "dynamic_ready",
+                                   "dynamic_static"])
 def test_full_size_block_cover(ws, T, sched):
     cfg = synth.MOE_PRESETS[NAME]
     wg, wu, wd = moe_weights(NAME)
     logits, x = synth.moe_activations(cfg, T, device=DEV)
     out = torch.full((T, cfg["hidden"]), float("nan"), device=DEV)
     say("moe_large", T, sched)
-    et.moe_layer(logits, x, wg, wu, wd, out, ws, sched)
+    if sched.startswith("dynamic_"):
+        et.moe_layer(logits, x, wg, wu, wd, out, ws, "dynamic", queue_order=sched[8:])
+    else:
+        et.moe_layer(logits, x, wg, wu, wd, out, ws, sched)
     torch.cuda.synchronize()
     st = ws.status()
     assert st["status"] == 0, st
