@@ -31,6 +31,7 @@ RunArgs LaunchCommon::run_args() const {
   a.phase = -1;
   a.timeout = (debug & ET_DEBUG_WATCHDOG_TICK) ? 1 : (long long)timeout_ms * 100000ll;
   a.n_init = 0;
+  a.impl_base = 0;
   a.total_hint = kUnknownTotal;
   a.extent = 0;
   return a;
@@ -44,7 +45,7 @@ __global__ void ws_init_kernel(int* ws, size_t words, int workload) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < words;
        i += (size_t)gridDim.x * blockDim.x)
     ws[i] = i == HDR_MAGIC ? kMagic : i == HDR_WORKLOAD ? workload
-          : i == HDR_QTOTAL ? kUnknownTotal : 0;
+          : i == HDR_QTOTAL || i == HDR_QIMPL ? kUnknownTotal : 0;
 }
 
 namespace {

@@ -82,6 +82,8 @@ struct RunArgs {
   long long timeout;   // watchdog, 100 MHz ticks
   int init_base;       // dynamic: tasks [0, init_base) run on workgroups w, w + G, ... directly
   int n_init;          // dynamic: tasks [init_base, init_base + n_init) are in the queue from the start
+  int impl_base;       // dynamic: > 0: static-order implicit tasks impl_base + p, p < HDR_QIMPL
+                       // (published during the call), ahead of each shard's pushed slots
   int n_single;        // dynamic: slots below this index are claimed one at a time
   int total_hint;      // dynamic: total tasks when known at launch, else kUnknownTotal
   int extent;          // counters this call uses (a prefix of its bank)
@@ -400,6 +402,8 @@ struct PopState {
   int pre_base = 0;      // that claim's first index (its atomic's return value)
   int pre_size = 0;      // its size; 0: none outstanding
   int pre_pushed = 0;    // the shard's push counter read beside that atomic
+  int impl = -1;         // static-order implicit tasks of this worker's shard (-1: not yet known)
+  int impl_all = 0;      // ... of all shards
 };
 
 // Implicit initial tasks of shard q: ids q, q + nq, ... below n_init.
@@ -407,16 +411,40 @@ __device__ __forceinline__ int shard_init(const RunArgs& a, int q) {
   return a.n_init > q ? (a.n_init - q + a.nq - 1) / a.nq : 0;
 }
 
+// Static-order implicit tasks (RunArgs.impl_base > 0): the call's n tasks
+// impl_base + p, p < n, published as a count in HDR_QIMPL.  Shard q holds, in
+// order, the positions its XCD runs under the static schedule: with G a
+// multiple of 8, G/8 consecutive positions per XCD and round (XCD (p mod G) /
+// (G/8)); otherwise positions p with (p mod G) mod 8 = q; one shard: all.
+__device__ __forceinline__ int impl_count(const Ctx& c, int q, int n) {
+  if (c.a.nq == 1) return n;
+  const int G = c.G, R = n / G, rem = n % G;
+  if (G % 8 == 0) {
+    const int per = G / 8;
+    return R * per + min(per, max(0, rem - q * per));
+  }
+  return R * ((G - q + 7) / 8) + (rem > q ? (rem - q + 7) / 8 : 0);
+}
+__device__ __forceinline__ int impl_task(const Ctx& c, int q, int idx) {
+  if (c.a.nq == 1) return c.a.impl_base + idx;
+  const int G = c.G;
+  if (G % 8 == 0) {
+    const int per = G / 8;
+    return c.a.impl_base + (idx / per) * G + q * per + idx % per;
+  }
+  const int pr = (G - q + 7) / 8;
+  return c.a.impl_base + (idx / pr) * G + q + 8 * (idx % pr);
+}
+
 // Thread 0: slot index idx of this worker's shard -> task id; -1 when the
 // call has no more tasks for this shard, -2 on a fault.  Index space of a
-// shard: its implicit initial tasks, then its pushed slots.  A claimed slot
-// that is not yet written is waited for; it is given up once every task of
-// the call has been pushed and the index lies beyond what this shard
-// received.
-__device__ __forceinline__ int resolve_slot(const Ctx& c, int q, int idx) {
+// shard: its implicit tasks (n_init of them, n_all over all shards), then
+// its pushed slots.  A claimed slot that is not yet written is waited for;
+// it is given up once every task of the call has been pushed and the index
+// lies beyond what this shard received.
+__device__ __forceinline__ int resolve_slot(const Ctx& c, int q, int idx, int n_init, int n_all) {
   const RunArgs& a = c.a;
-  const int n_init = shard_init(a, q);
-  if (idx < n_init) return a.init_base + q + a.nq * idx;
+  if (idx < n_init) return a.impl_base > 0 ? impl_task(c, q, idx) : a.init_base + q + a.nq * idx;
   const int s = idx - n_init;
   int* p = &a.slots[(size_t)q * a.q_cap + s];
   long long t0 = 0;
@@ -441,7 +469,7 @@ __device__ __forceinline__ int resolve_slot(const Ctx& c, int q, int idx) {
             pushed += v;
             if (j == q) mine = v;
           }
-          if (a.n_init + pushed >= total && s >= mine) return -1;
+          if (n_all + pushed >= total && s >= mine) return -1;
         }
       }
     }
@@ -481,54 +509,81 @@ __device__ __forceinline__ int wg_pop(const Ctx& c, PopState& ps) {
   if (threadIdx.x == 0) {
     const RunArgs& a = c.a;
     const int q = c.wg % a.nq;
-    const int n_init = shard_init(a, q);
-    int* head = q_claimed(a, q);
-    if (ps.left == 0) {
-      if (ps.pre_size > 0) {
-        ps.base = ps.pre_base;
-        ps.size = ps.left = ps.pre_size;
-        ps.pre_size = 0;
-        const int per = c.G / a.nq > 0 ? c.G / a.nq : 1;
-        ps.ahead = n_init + ps.pre_pushed - (ps.base + ps.size) >= 3 * per * a.fetch;
-      } else {
-        const int h = ld_rlx(head);
-        const int avail = n_init + ld_rlx(q_pushed(a, q)) - h;
-        const int per = c.G / a.nq > 0 ? c.G / a.nq : 1;
-        int sz = avail / per;
-        sz = h * a.nq < a.n_single ? 1 : (sz < 1 ? 1 : (sz > a.fetch ? a.fetch : sz));
-        ps.ahead = sz == a.fetch && avail >= 3 * per * a.fetch;
-        ps.base = add_rlx(head, sz);
-        ps.size = ps.left = sz;
+    bool stop = false;
+    if (a.impl_base > 0 && ps.impl < 0) {
+      // static-order implicit tasks: wait until the call has published their
+      // count (the scan does, early in the call); a fault ends the worker
+      const long long t0 = now_ticks();
+      int n = ld_rlx(&a.hdr[HDR_QIMPL]);
+      for (int it = 1; n == kUnknownTotal; ++it) {
+        __builtin_amdgcn_s_sleep(1);
+        n = ld_rlx(&a.hdr[HDR_QIMPL]);
+        if (n == kUnknownTotal && ((it & 63) == 0 || a.timeout <= 1)) {
+          if (faulted(a)) break;
+          if (now_ticks() - t0 > a.timeout) {
+            raise_fault(a, ET_ETIMEOUT, -1, HDR_QIMPL, q);
+            break;
+          }
+        }
       }
-      int v[kMaxFetch];
-#pragma unroll
-      for (int i = 0; i < kMaxFetch; ++i) {
-        const int sl = ps.base + i - n_init;
-        v[i] = (i < ps.size && sl >= 0 && sl < a.q_cap) ? ld_rlx(&a.slots[(size_t)q * a.q_cap + sl]) : 0;
-      }
-#pragma unroll
-      for (int i = 0; i < kMaxFetch; ++i)
-        if (i < ps.size) c.sh->bids[i] = v[i];
-    }
-    const int k = ps.size - ps.left;
-    const int idx = ps.base + k;
-    --ps.left;
-    if (idx < n_init) {
-      t = a.init_base + q + a.nq * idx;
-    } else {
-      const int v = c.sh->bids[k];
-      if (v != 0) {
-        st_rlx(&a.slots[(size_t)q * a.q_cap + (idx - n_init)], 0);   // empty for the next call
-        t = v - 1;
+      if (n == kUnknownTotal) {
+        stop = true;
       } else {
-        t = resolve_slot(c, q, idx);   // not yet written when read: wait for it
-        if (t < 0) t = -1;
+        ps.impl = impl_count(c, q, n);
+        ps.impl_all = n;
       }
     }
-    if (ps.left == 0 && ps.ahead && t >= 0) {
-      ps.pre_base = add_rlx(head, a.fetch);
-      ps.pre_pushed = ld_rlx(q_pushed(a, q));
-      ps.pre_size = a.fetch;
+    if (!stop) {
+      const int n_init = a.impl_base > 0 ? ps.impl : shard_init(a, q);
+      const int n_all = a.impl_base > 0 ? ps.impl_all : a.n_init;
+      int* head = q_claimed(a, q);
+      if (ps.left == 0) {
+        if (ps.pre_size > 0) {
+          ps.base = ps.pre_base;
+          ps.size = ps.left = ps.pre_size;
+          ps.pre_size = 0;
+          const int per = c.G / a.nq > 0 ? c.G / a.nq : 1;
+          ps.ahead = n_init + ps.pre_pushed - (ps.base + ps.size) >= 3 * per * a.fetch;
+        } else {
+          const int h = ld_rlx(head);
+          const int avail = n_init + ld_rlx(q_pushed(a, q)) - h;
+          const int per = c.G / a.nq > 0 ? c.G / a.nq : 1;
+          int sz = avail / per;
+          sz = h * a.nq < a.n_single ? 1 : (sz < 1 ? 1 : (sz > a.fetch ? a.fetch : sz));
+          ps.ahead = sz == a.fetch && avail >= 3 * per * a.fetch;
+          ps.base = add_rlx(head, sz);
+          ps.size = ps.left = sz;
+        }
+        int v[kMaxFetch];
+#pragma unroll
+        for (int i = 0; i < kMaxFetch; ++i) {
+          const int sl = ps.base + i - n_init;
+          v[i] = (i < ps.size && sl >= 0 && sl < a.q_cap) ? ld_rlx(&a.slots[(size_t)q * a.q_cap + sl]) : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < kMaxFetch; ++i)
+          if (i < ps.size) c.sh->bids[i] = v[i];
+      }
+      const int k = ps.size - ps.left;
+      const int idx = ps.base + k;
+      --ps.left;
+      if (idx < n_init) {
+        t = a.impl_base > 0 ? impl_task(c, q, idx) : a.init_base + q + a.nq * idx;
+      } else {
+        const int v = c.sh->bids[k];
+        if (v != 0) {
+          st_rlx(&a.slots[(size_t)q * a.q_cap + (idx - n_init)], 0);   // empty for the next call
+          t = v - 1;
+        } else {
+          t = resolve_slot(c, q, idx, n_init, n_all);   // not yet written when read: wait for it
+          if (t < 0) t = -1;
+        }
+      }
+      if (ps.left == 0 && ps.ahead && t >= 0) {
+        ps.pre_base = add_rlx(head, a.fetch);
+        ps.pre_pushed = ld_rlx(q_pushed(a, q));
+        ps.pre_size = a.fetch;
+      }
     }
   }
   return wg_bcast(c, t, 4);
@@ -604,6 +659,7 @@ __device__ __forceinline__ void epilogue(const Ctx& c, int tasks_this_call) {
         st_rlx(q_pushed(c.a, q), 0);
       }
       st_rlx(&h[HDR_QTOTAL], kUnknownTotal);
+      st_rlx(&h[HDR_QIMPL], kUnknownTotal);
       st_rlx(&h[HDR_EXT0 + bank], c.a.extent);
       st_rlx(&h[HDR_LAST_TASKS], tasks_this_call);
       st_rlx(&h[HDR_CALLS], ld_rlx(&h[HDR_CALLS]) + 1);

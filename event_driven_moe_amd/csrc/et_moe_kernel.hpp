@@ -101,9 +101,10 @@ constexpr int kInlineCombineTokens = 4;
 constexpr int kSoloPush = 4;
 // Dynamic schedule, ET_QORDER_AUTO: the static-order queue from this many
 // GEMM tasks per worker on (moe_large T = 2048 / 8192 dynamic: 4.03 / 8.06 ms
-// with tasks pushed as they become ready, 3.83 / 7.68 ms in static order with
-// one-slot claims; moe_skewed T = 1024, 5 tasks per worker: 220 us against
-// 233 us, where the ready order wins).
+// with tasks pushed as they become ready, 3.82 / 7.67 ms in static order with
+// one-entry claims, against 3.74-3.76 / 7.52-7.53 ms static; moe_skewed
+// T = 1024, 5 tasks per worker: 220 us against 233 us, where the ready order
+// wins).
 constexpr int kQAllTasks = 16;
 constexpr int kIdxCache = 2 * (kMaxExperts + 1) * 4;   // tok_indptr + blk_indptr copies
 constexpr int kGenBytes = kGenIdx + kIdxCache;
@@ -1248,6 +1249,20 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
           wg_release();
           t0_notify_bcast(c, EV_SCAN, EV_SCAN, 1, 1, NR);
         }
+        if (sched == ET_SCHED_DYNAMIC && m.qall) {
+          // Static-order queue: the GEMM tasks base1 + p, p < nb (nt1 + nt2)
+          // (every gate/up task, then every down task), become implicit
+          // entries of the shards, each position in the shard of the XCD the
+          // static schedule runs it on, in order -- a shard's consecutive
+          // entries are the row blocks sharing one weight tile.  Publishing
+          // their count is the push.  Every gate/up task precedes every down
+          // task in each shard and a down task waits only on gate/up tasks,
+          // so a worker waiting on a claimed down task holds back no task it
+          // waits for.  Gate/up tasks still wait on their expert's E_exp.
+          if (!many_chunks) wg_release();
+          set_total(c, nb * (nt1 + nt2) + ncomb + (kBlock ? n_mg + n_md : 0));
+          if (tid == 0) st_rlx(&c.a.hdr[HDR_QIMPL], nb * (nt1 + nt2));
+        }
       }
       if (sched == ET_SCHED_DYNAMIC) {
         // Early push (the appendix of the dynamic schedule: consumers are
@@ -1318,21 +1333,6 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
           const int old = add_rlx(c.ev + m.ev_exp + e, -n);
           if (old - n < -wcnt) raise_fault(ra, ET_ESTATE, task, m.ev_exp + e, old - n);
         }
-      }
-      if (m.qall && task == 0) {
-        // Static-order queue: chunk 0, its own tokens grouped, pushes every
-        // gate/up task and then every down task in task-id order, position
-        // p = id - base1 to the shard of the XCD the static schedule runs p
-        // on (XCD (p mod G) / (G / 8): G / 8 consecutive positions per XCD
-        // and round), so a shard's consecutive slots are the row blocks
-        // sharing one weight tile.  Every gate/up task precedes every
-        // down task in each shard and a down task waits only on gate/up
-        // tasks, so a worker that waits on a claimed down task never holds
-        // back a task it waits for.
-        wg_release();
-        const int per = c.G / 8;
-        wg_push(c, nb * (nt1 + nt2), [&](int i) { return base1 + i; },
-                [&](int i) { return c.G % 8 == 0 ? (i % c.G) / per : (i % c.G) % 8; });
       }
       return true;
     }
@@ -1491,7 +1491,11 @@ inline int moe_setup(const LaunchCommon& lc, const MoePlan& mp, const MoeAux& ax
   ra = lc.run_args();
   ra.init_base = m.NR;   // dynamic: routing runs on workgroups 0..NR-1
   ra.n_init = 0;         // the queue holds pushed tasks only
-  ra.n_single = m.qall ? (1 << 30) : 0;   // static order: every claim takes one slot
+  ra.n_single = 0;
+  if (m.qall) {
+    ra.impl_base = 2 * m.NR + 1;   // the first gate/up task
+    ra.fetch = 1;                  // claims of one entry: the blocks of a weight tile side by side
+  }
   ra.total_hint = kUnknownTotal;
   ra.extent = mp.extent(T, tl);
   return ET_OK;

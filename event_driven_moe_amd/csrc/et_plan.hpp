@@ -31,6 +31,7 @@ enum : int {
   HDR_ERR_B = 66,
   HDR_ERR_C = 67,
   HDR_QHEAD = 96,       // ready queue: implicit initial tasks claimed
+  HDR_QIMPL = 128,      // ready queue: static-order implicit tasks of this call once known (else INT_MAX)
   HDR_QTOTAL = 160,     // ready queue: total tasks of this call once known (else INT_MAX)
   HDR_EXIT = 192,       // workgroups that finished this call
   HDR_META = 224,       // 32 words of per-call workload metadata

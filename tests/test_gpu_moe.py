@@ -106,12 +106,13 @@ def test_tile_variants(tile, sched, T):
 @pytest.mark.parametrize("name,T", [("moe_small", 8), ("moe_small", 32), ("moe_skewed", 64),
                                     ("moe_skewed", 1024), ("moe_skewed_cal", 256)])
 @pytest.mark.parametrize("tile", [-1, 3, 4])
-@pytest.mark.parametrize("fetch", [1, 8])
-def test_static_order_queue(name, T, tile, fetch):
-    """Dynamic schedule with every GEMM task queued at the scan in the static
-    order (claims of one slot whatever the fetch batch), on every tile kind."""
+@pytest.mark.parametrize("fetch,shards", [(1, 0), (8, 0), (2, 1)])
+def test_static_order_queue(name, T, tile, fetch, shards):
+    """Dynamic schedule with every GEMM task an implicit queue entry in the
+    static order (claims of one entry whatever the fetch batch), on every tile
+    kind, with per-XCD shards and with one central queue."""
     _, _, _, _, out, aux, _ = run_moe(name, T, "dynamic", queue_order="static", tile=tile,
-                                      fetch_batch=fetch)
+                                      fetch_batch=fetch, queue_shards=shards)
     check_against_oracle(name, T, out, aux, tile)
 
 
