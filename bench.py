@@ -157,22 +157,43 @@ def kernel_stats(db):
             100.0 * sum(d) / total, "/".join(str(x) for x in r["res"])))
 
 
+SKIP_DISPATCHES = 2   # the untimed first call and the first warm-up call
+
+
+def traffic_entry(per_counter):
+    """{counter: (MoE kernel KiB per dispatch in launch order, calibration copy
+    KiB per dispatch)} -> the stored traffic record.  The first
+    SKIP_DISPATCHES launches (first touch of the workspace and weights, and
+    the first warm-up call, which read 10-30% more) are left out, so the
+    figure belongs to launches like the timed ones."""
+    res = {}
+    for name, (moe, cpy) in per_counter.items():
+        if len(moe) <= SKIP_DISPATCHES or not cpy:
+            raise SystemExit("%s: need more than %d MoE kernel dispatches and a calibration copy"
+                             % (name, SKIP_DISPATCHES))
+        used = moe[SKIP_DISPATCHES:]
+        cal = COPY_BYTES / (1024.0 * sum(cpy) / len(cpy))
+        res[name] = {"kib_per_dispatch": sum(used) / len(used), "dispatches": len(used),
+                     "dispatches_skipped": SKIP_DISPATCHES, "copy_kib": sum(cpy) / len(cpy),
+                     "scale": cal, "bytes": 1024.0 * cal * sum(used) / len(used)}
+    return res
+
+
 def traffic_summary(fetch_db, write_db, key):
     """HBM bytes per launch of the MoE kernel from a FETCH_SIZE run and a
     WRITE_SIZE run (both KiB per dispatch), each scaled by what the counter
     reads for the calibration copy; stores the figure for later bench lines."""
-    res = {}
+    per = {}
     for name, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
         d = _pmc_per_dispatch(db, name)
         moe = [v for k, vs in d.items() if "moe_kernel" in k for v in vs]
         cpy = [v for k, vs in d.items() if "moe_kernel" not in k for v in vs
                if abs(v * 1024 - COPY_BYTES) < 0.6 * COPY_BYTES]
-        if not moe or not cpy:
-            raise SystemExit("%s: no MoE kernel or calibration copy dispatches in %s" % (name, db))
-        cal = COPY_BYTES / (1024.0 * sum(cpy) / len(cpy))
-        res[name] = {"kib_per_dispatch": sum(moe) / len(moe), "dispatches": len(moe),
-                     "copy_kib": sum(cpy) / len(cpy), "scale": cal,
-                     "bytes": 1024.0 * cal * sum(moe) / len(moe)}
+        per[name] = (moe, cpy)
+    store_traffic(key, traffic_entry(per))
+
+
+def store_traffic(key, res):
     ent = {"kernel_hash": kernel_source_hash(),
            "hbm_bytes_per_launch": int(res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"]),
            "read_bytes": int(res["FETCH_SIZE"]["bytes"]), "write_bytes": int(res["WRITE_SIZE"]["bytes"]),
@@ -380,6 +401,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=8192)
     ap.add_argument("--sched", default="static")
     ap.add_argument("--fetch", type=int, default=2)
+    ap.add_argument("--queue-order", default="auto", choices=("auto", "ready", "static"),
+                    help="dynamic schedule of the MoE GEMM tasks (et_opts.queue_order)")
     ap.add_argument("--no-modes", action="store_true",
                     help="time only --sched (default: every schedule, reported in config)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -434,10 +457,10 @@ def main():
                                for _ in range(weight_copies(args, 3 * wg.numel() * 2) - 1)]
     turn = [0]
 
-    def step(sched=args.sched):
+    def step(sched=args.sched, order=args.queue_order):
         g, u, d = copies[turn[0] % len(copies)]
         turn[0] += 1
-        et.moe_layer(logits, x, g, u, d, out, ws, sched, fetch_batch=args.fetch)
+        et.moe_layer(logits, x, g, u, d, out, ws, sched, fetch_batch=args.fetch, queue_order=order)
 
     step()
     torch.cuda.synchronize()
@@ -488,7 +511,7 @@ def main():
     # workgroup's real-time and shader-clock stamps at start and end
     g, u, d = copies[0]
     et.moe_layer(logits, x, g, u, d, out, ws, args.sched, fetch_batch=args.fetch,
-                 debug=et.DEBUG_CLOCK)
+                 queue_order=args.queue_order, debug=et.DEBUG_CLOCK)
     torch.cuda.synchronize()
     stamps = ws.clock_stamps()[: et.num_workers()].cpu().long()
     d_rt = (stamps[:, 1, 0] - stamps[:, 0, 0]) & 0xFFFFFFFF
@@ -497,9 +520,12 @@ def main():
 
     modes = {}
     if not args.no_modes:
-        for s in ("static", "dynamic", "barrier", "per_op"):
+        for s, order in (("static", "auto"), ("dynamic", "auto"), ("dynamic_ready", "ready"),
+                         ("dynamic_static_order", "static"), ("barrier", "auto"),
+                         ("per_op", "auto")):
             log("bench: timing schedule %s" % s)
-            p, _ = time_calls(lambda: step(s), max(10, args.steps // 2), 3)
+            p, _ = time_calls(lambda: step(s.split("_")[0] if s.startswith("dynamic") else s, order),
+                              max(10, args.steps // 2), 3)
             modes[s] = round(1e3 * sum(p) / len(p), 2)
         if ws.status()["status"] != 0:
             raise SystemExit("device fault while timing the schedules")
@@ -517,8 +543,10 @@ def main():
                                                cfg["top_k"], cfg["inter"], bias),
             "tokens": T, "schedule": args.sched,
             "fetch_batch_cap": args.fetch,
-            "fetch_batch_note": "dynamic schedule: at most this many queue slots per claim; a "
-                                "claim takes no more than the worker's share of the published slots",
+            "fetch_batch_note": "dynamic schedule, ready order: at most this many queue slots per "
+                                "claim, and no more than the worker's share of the published slots; "
+                                "static order: one entry per claim",
+            "queue_order": args.queue_order,
             "active_experts": n_active, "max_rows_per_expert": max_rows,
             "us_per_layer_mean": round(1e3 * ms, 2),
             "us_per_layer_median": round(1e3 * per_sorted[len(per) // 2], 2),
@@ -544,9 +572,13 @@ def main():
     }
     if modes:
         res["config"]["us_per_layer_by_schedule"] = modes
-        res["config"]["schedules"] = ("static: per-CU task lists; dynamic: on-device ready queue; "
-                                      "barrier: same tasks, one event per operator; per_op: one "
-                                      "kernel launch per operator")
+        res["config"]["schedules"] = ("static: per-CU task lists; dynamic: on-device ready queue "
+                                      "(queue order chosen by the library: the static order from 16 "
+                                      "GEMM tasks per worker on the 64- and 128-row tiles, else "
+                                      "tasks pushed as they become ready); dynamic_ready / "
+                                      "dynamic_static_order: one queue order forced; barrier: same "
+                                      "tasks, one event per operator; per_op: one kernel launch per "
+                                      "operator")
     if not args.no_cpu:
         log("bench: oracle CPU baseline")
         res["cpu_baseline"] = cpu_baseline(cfg, logits, x, wg, wu, wd, T)

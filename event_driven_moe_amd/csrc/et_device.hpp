@@ -543,14 +543,18 @@ __device__ __forceinline__ int wg_pop(const Ctx& c, PopState& ps) {
           ps.size = ps.left = ps.pre_size;
           ps.pre_size = 0;
           const int per = c.G / a.nq > 0 ? c.G / a.nq : 1;
-          ps.ahead = n_init + ps.pre_pushed - (ps.base + ps.size) >= 3 * per * a.fetch;
+          ps.ahead = n_init + ps.pre_pushed - (ps.base + ps.size) >= 3 * per * ps.size;
         } else {
           const int h = ld_rlx(head);
           const int avail = n_init + ld_rlx(q_pushed(a, q)) - h;
           const int per = c.G / a.nq > 0 ? c.G / a.nq : 1;
+          // static-order implicit entries are claimed one at a time: a
+          // shard's consecutive entries are the row blocks sharing a weight
+          // tile, which should run side by side on different workers
+          const int cap = a.impl_base > 0 && h < n_init ? 1 : a.fetch;
           int sz = avail / per;
-          sz = h * a.nq < a.n_single ? 1 : (sz < 1 ? 1 : (sz > a.fetch ? a.fetch : sz));
-          ps.ahead = sz == a.fetch && avail >= 3 * per * a.fetch;
+          sz = h * a.nq < a.n_single ? 1 : (sz < 1 ? 1 : (sz > cap ? cap : sz));
+          ps.ahead = sz == cap && avail >= 3 * per * cap;
           ps.base = add_rlx(head, sz);
           ps.size = ps.left = sz;
         }
@@ -580,9 +584,11 @@ __device__ __forceinline__ int wg_pop(const Ctx& c, PopState& ps) {
         }
       }
       if (ps.left == 0 && ps.ahead && t >= 0) {
-        ps.pre_base = add_rlx(head, a.fetch);
+        // (the head is at least base + size: a lower bound picks the cap)
+        const int cap = a.impl_base > 0 && ps.base + ps.size < n_init ? 1 : a.fetch;
+        ps.pre_base = add_rlx(head, cap);
         ps.pre_pushed = ld_rlx(q_pushed(a, q));
-        ps.pre_size = a.fetch;
+        ps.pre_size = cap;
       }
     }
   }

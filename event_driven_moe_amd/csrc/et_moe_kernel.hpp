@@ -78,7 +78,8 @@ struct MoeArgs {
   float* y2;           // [T, H] dense MLP output
   int Im;
   int ev_z, ev_hm;     // E_z[mb] (combine tiles of row block mb), E_hm[mb][Im / 128]
-  int qall;   // dynamic: every GEMM task queued at the scan in static order (ET_QORDER_STATIC)
+  int qall;   // dynamic: the static-order queue may be chosen (queue order auto or static)
+  int qforce; // dynamic: ... and is chosen whatever the routing (queue order static)
 };
 
 // LDS: three slot arrays (the GEMM ring of the wide variants; scratch for
@@ -99,13 +100,6 @@ constexpr int kInlineCombineTokens = 4;
 // Dynamic schedule: with at most this many gate/up tasks per workgroup, routing
 // chunk 0 alone pushes them (early push); with more, every chunk pushes a share.
 constexpr int kSoloPush = 4;
-// Dynamic schedule, ET_QORDER_AUTO: the static-order queue from this many
-// GEMM tasks per worker on (moe_large T = 2048 / 8192 dynamic: 4.03 / 8.06 ms
-// with tasks pushed as they become ready, 3.82 / 7.67 ms in static order with
-// one-entry claims, against 3.74-3.76 / 7.52-7.53 ms static; moe_skewed
-// T = 1024, 5 tasks per worker: 220 us against 233 us, where the ready order
-// wins).
-constexpr int kQAllTasks = 16;
 constexpr int kIdxCache = 2 * (kMaxExperts + 1) * 4;   // tok_indptr + blk_indptr copies
 constexpr int kGenBytes = kGenIdx + kIdxCache;
 
@@ -290,8 +284,12 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
   int* c_tok = reinterpret_cast<int*>(gen + kGenIdx);
   int* c_blk = c_tok + kMaxExperts + 1;
   bool cached = false;
+  // dynamic: this call's GEMM tasks are static-order queue entries (the scan's
+  // choice; known to every task once the scan results are out)
+  bool qs = false;
   auto load_cache = [&]() ET_INLINE {
     if (cached) return;
+    if (m.qall) qs = ld_rlx(&ra.hdr[HDR_META + MD_QSTATIC]) != 0;
     for (int e = tid; e <= m.E; e += kThreads) {
       c_tok[e] = ld_coh(&m.tok_indptr[e]);
       c_blk[e] = ld_coh(&m.blk_indptr[e]);
@@ -805,6 +803,25 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       }
       s_i[e] = s_i[1024 + e] = cnt[e] + bef[e];   // hs is no longer read
     }
+    if (m.qall) {
+      // Dynamic queue order: the static order, unless one expert is chosen
+      // by at least 90% of the tokens and holds at least 4 row blocks --
+      // then the many down tasks waiting on that expert's blocks would each
+      // hold a worker still while ready tasks sit behind them in the shard,
+      // and tasks pushed as they become ready do better (moe_skewed, every
+      // token routed to one expert: T = 256 / 1024 135 / 220 us against
+      // 147 / 223 us in static order; the static order wins at every other
+      // size measured, by 2-10%: moe_small, moe_skewed_cal, moe_large).
+      int mr = 0;
+      for (int e = tid; e < m.E; e += kThreads)
+        if ((e + 1 < m.E ? blk[e + 1] : nb) - blk[e] >= 4)
+          mr = max(mr, (e + 1 < m.E ? cnt[e + 1] : m.T * m.k) - cnt[e]);
+      mr = (int)wave_reduce_u32<true>((uint32_t)mr);
+      if (lane == 0) tmp[wave] = mr;
+      lds_barrier();
+      mr = max(max(tmp[0], tmp[1]), max(tmp[2], tmp[3]));
+      qs = m.qforce || 10 * mr < 9 * m.T;
+    }
     if (pub && tid == 0) {
       st_coh(&m.tok_indptr[m.E], m.T * m.k);
       st_coh(&m.blk_indptr[m.E], nb);
@@ -812,6 +829,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
       st_rlx(&ra.hdr[HDR_META + MD_NB], nb);
       st_rlx(&ra.hdr[HDR_META + MD_TOTAL1], nb * nt1);
       st_rlx(&ra.hdr[HDR_META + MD_TOTAL2], nb * nt2);
+      st_rlx(&ra.hdr[HDR_META + MD_QSTATIC], qs ? 1 : 0);
     }
     lds_barrier();
     return nb;
@@ -918,7 +936,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     wg_release();
     if (sched == ET_SCHED_BARRIER) {
       t0_notify_bcast(c, EV_G1ALL, EV_G1ALL, 1, meta(MD_TOTAL1), task);
-    } else if (sched == ET_SCHED_STATIC || m.qall) {
+    } else if (sched == ET_SCHED_STATIC || qs) {
       t0_notify(c, m.ev_h + gb, 1, nt1, task);
     } else {
       // dynamic: the expert's event counts its gate/up tiles over all of its
@@ -962,7 +980,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
     const Rsrc rh = make_rsrc(m.h, (uint32_t)m.T * m.k * m.I * 2);
     auto gate = [&](int round) ET_INLINE -> bool {
       if (round != 0) return true;
-      if (sched == ET_SCHED_STATIC || m.qall) {
+      if (sched == ET_SCHED_STATIC || qs) {
         if (!wg_wait(c, m.ev_h + gb, nt1, task)) return false;
       } else if (sched == ET_SCHED_BARRIER && !seen_g1) {
         if (!wg_wait_bcast(c, EV_G1ALL, EV_G1ALL, task)) return false;
@@ -1259,9 +1277,11 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
           // task in each shard and a down task waits only on gate/up tasks,
           // so a worker waiting on a claimed down task holds back no task it
           // waits for.  Gate/up tasks still wait on their expert's E_exp.
+          // (Ready order chosen: the count is 0 and the queue holds pushed
+          // tasks only.)
           if (!many_chunks) wg_release();
           set_total(c, nb * (nt1 + nt2) + ncomb + (kBlock ? n_mg + n_md : 0));
-          if (tid == 0) st_rlx(&c.a.hdr[HDR_QIMPL], nb * (nt1 + nt2));
+          if (tid == 0) st_rlx(&c.a.hdr[HDR_QIMPL], qs ? nb * (nt1 + nt2) : 0);
         }
       }
       if (sched == ET_SCHED_DYNAMIC) {
@@ -1282,7 +1302,7 @@ __global__ __launch_bounds__(kThreads, MoeCfg<TV>::kOcc) void moe_kernel(RunArgs
         if (task == 0) set_total(c, nb * (nt1 + nt2) + ncomb + (kBlock ? n_mg + n_md : 0));
         const int total1 = nb * nt1;
         const bool solo_push = total1 <= kSoloPush * c.G;
-        if (!m.qall && (!solo_push || task == 0)) {
+        if (!qs && (!solo_push || task == 0)) {
           wg_release();
           if (task != 0 && many_chunks && !wg_wait_bcast(c, EV_SCAN, EV_SCAN, task)) return false;
           const int* blk = reinterpret_cast<const int*>(s1) + 1024;   // exclusive block offsets
@@ -1480,22 +1500,16 @@ inline int moe_setup(const LaunchCommon& lc, const MoePlan& mp, const MoeAux& ax
   m.ev_he = mp.ev_he();
   m.ev_h = mp.ev_h();
   m.ev_c = mp.ev_c();
-  // static-order queue (dynamic schedule): forced, or for the wide tiles
-  // when the call has at least kQAllTasks GEMM tasks per worker (counting
-  // each expert's rows as full blocks, a lower bound)
-  const bool wide = tv == TV_W64 || tv == TV_W128;
-  const long long est_tasks = (long long)T * m.k / (16 * tl.mt) * (m.I / tl.bn1 + m.H / tl.bn2);
-  m.qall = lc.sched == ET_SCHED_DYNAMIC &&
-           (lc.qorder == ET_QORDER_STATIC ||
-            (lc.qorder == ET_QORDER_AUTO && wide && est_tasks >= (long long)kQAllTasks * lc.G));
+  // dynamic schedule: the static-order queue may be chosen by the scan
+  // (queue order auto) or is forced (static); implicit entries from the first
+  // gate/up task on
+  m.qall = lc.sched == ET_SCHED_DYNAMIC && lc.qorder != ET_QORDER_READY;
+  m.qforce = lc.sched == ET_SCHED_DYNAMIC && lc.qorder == ET_QORDER_STATIC;
   ra = lc.run_args();
   ra.init_base = m.NR;   // dynamic: routing runs on workgroups 0..NR-1
   ra.n_init = 0;         // the queue holds pushed tasks only
   ra.n_single = 0;
-  if (m.qall) {
-    ra.impl_base = 2 * m.NR + 1;   // the first gate/up task
-    ra.fetch = 1;                  // claims of one entry: the blocks of a weight tile side by side
-  }
+  if (m.qall) ra.impl_base = 2 * m.NR + 1;   // the first gate/up task
   ra.total_hint = kUnknownTotal;
   ra.extent = mp.extent(T, tl);
   return ET_OK;

@@ -158,7 +158,7 @@ enum : int { EV_ROUTE = 0, EV_SCAN = 1, EV_GROUP = 2, EV_G1ALL = 3, EV_DOWN = 4,
              EV_MG = 6, EV_FIXED = 8 };
 
 // per-call metadata words (HDR_META + i), written by the scan task
-enum : int { MD_NB = 0, MD_TOTAL1 = 1, MD_TOTAL2 = 2 };
+enum : int { MD_NB = 0, MD_TOTAL1 = 1, MD_TOTAL2 = 2, MD_QSTATIC = 3 };
 
 struct MoePlan {
   int t_max, hidden, inter, n_experts, top_k, n_route;

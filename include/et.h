@@ -117,15 +117,18 @@ typedef struct et_opts {
  * READY: the scan pushes every gate/up task early (each waits on its expert's
  *   grouping event, E_exp); the notify that completes an expert's gate/up
  *   tiles (E_he) pushes its down tasks, which enter the queue ready to run.
- * STATIC: once its grouping is done, routing chunk 0 pushes every gate/up and
- *   down task in the static schedule's order, each to the shard of the XCD
- *   the static schedule would run it on; down tasks wait on their row block's
- *   E_h event, and claims take one slot (the consecutive slots of a shard are
- *   the row blocks sharing a weight tile, which then stream it side by side).
- *   The early-push form of the dynamic schedule (Event Tensor notes, section
- *   on dynamic scheduling and its appendix).
- * AUTO: STATIC for the 128- and 64-row GEMM tiles when the call has at least
- *   16 GEMM tasks per worker, else READY. */
+ * STATIC: once the scan knows the row blocks, every gate/up task and then
+ *   every down task becomes a queue entry in the static schedule's order, in
+ *   the shard of the XCD the static schedule would run it on (the scan
+ *   publishes their count; no slots are written); gate/up tasks wait on
+ *   E_exp, down tasks on their row block's E_h, and these entries are claimed
+ *   one at a time (a shard's consecutive entries are the row blocks sharing a
+ *   weight tile, which then stream it side by side).  The early-push form of
+ *   the dynamic schedule (Event Tensor notes, section on dynamic scheduling
+ *   and its appendix).
+ * AUTO: the scan picks, from the routing of the call: READY when one expert
+ *   is chosen by at least 90% of the tokens and holds at least 4 row blocks,
+ *   else STATIC. */
 enum {
   ET_QORDER_AUTO = 0,
   ET_QORDER_READY = 1,

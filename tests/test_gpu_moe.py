@@ -123,26 +123,35 @@ def test_fetch_batches(fetch):
 
 
 @pytest.mark.parametrize("T", [16, 64, 256, 1024])
-@pytest.mark.parametrize("sched", ["static", "dynamic", "dynamic_static"])
+@pytest.mark.parametrize("sched", ["static", "dynamic", "dynamic_ready", "dynamic_static"])
 def test_event_invariants(sched, T):
     """Each task ran once; the data-dependent expert events ended at their
     run-time wait counts (rows routed to each expert; dynamic, tasks pushed
     as they become ready: also the gate/up tiles over each expert's blocks),
     the block events (static schedule and the dynamic static-order queue) at
     the number of gate/up tiles of a block, and every combine tile's event at
-    its rows times overlapping down tiles."""
+    its rows times overlapping down tiles.  "dynamic" lets the scan choose
+    the queue order: ready when one expert is chosen by at least 90% of the
+    tokens and holds at least 4 row blocks, else static (the literal skew
+    preset routes every token to one expert, so the choice flips between
+    T = 64, one block, and T = 256)."""
     name = "moe_skewed"
     ws = _ws(name, 1024)
     ws.runs().zero_()
-    qstatic = sched == "dynamic_static"
-    if qstatic:
+    order = {"dynamic": "auto", "dynamic_ready": "ready", "dynamic_static": "static"}.get(sched, "auto")
+    if sched.startswith("dynamic"):
         sched = "dynamic"
     cfg, _, _, _, out, aux, _ = run_moe(name, T, sched, ws=ws, debug=et.DEBUG_COUNTS,
-                                        queue_order="static" if qstatic else "auto")
+                                        queue_order=order)
     st = ws.status()
     E, k, H, I = cfg["n_experts"], cfg["top_k"], cfg["hidden"], cfg["inter"]
     nr = min(128, 8192 // E, -(-T // 8))   # routing chunks of about 8 tokens
     rows, bn1, bn2 = moe_tiling(T, k)
+    cts = aux["counts"].astype(np.int64)
+    mr = int(cts[-(-cts // rows) >= 4].max(initial=0))
+    qstatic = order == "static" or (order == "auto" and not 10 * mr >= 9 * T)
+    if order == "auto":
+        assert qstatic == (T <= 64), (T, mr)
     ccols = 256 if -(-T // 16) * -(-H // 256) >= et.num_workers() else 64
     tab = oev.moe_table(aux["counts"], rows, I, bn1, H, bn2, nr, tokens=T, top_k=k,
                         comb_tok=16, comb_cols=ccols)
