@@ -573,9 +573,9 @@ def main():
     if modes:
         res["config"]["us_per_layer_by_schedule"] = modes
         res["config"]["schedules"] = ("static: per-CU task lists; dynamic: on-device ready queue "
-                                      "(queue order chosen by the library: the static order from 16 "
-                                      "GEMM tasks per worker on the 64- and 128-row tiles, else "
-                                      "tasks pushed as they become ready); dynamic_ready / "
+                                      "(queue order chosen per call by the scan from the routing: "
+                                      "the static schedule's order, or tasks pushed as they become "
+                                      "ready when one expert takes nearly every token); dynamic_ready / "
                                       "dynamic_static_order: one queue order forced; barrier: same "
                                       "tasks, one event per operator; per_op: one kernel launch per "
                                       "operator")
