@@ -50,7 +50,8 @@ enum {
                            (data-dependent MoE edges fall back to one coarse event, as the
                            static lowering of the Event Tensor notes does) */
   ET_SCHED_DYNAMIC = 1, /* on-device ready queue; the notify that zeroes an event pushes its
-                           consumers; workers claim `fetch_batch` queue slots per atomic */
+                           consumers, or consumers are queued early and wait on their event;
+                           workers claim up to `fetch_batch` queue slots per atomic */
   ET_SCHED_BARRIER = 2, /* same tasks and code, but one event per operator, i.e. a global
                            barrier between operators (the unfused-megakernel ablation baseline
                            of the Event Tensor notes, section "静态与动态调度的消融") */
@@ -245,9 +246,10 @@ int et_mlp(const uint16_t* x, int n_tokens, const uint16_t* w_gate, const uint16
  * -0.0 == +0.0) and renormalises their softmax weights to sum to 1.  Grouping is a
  * stable counting sort of (t, s) by expert.  Routing tensors, counts, CSR offsets and
  * the permutation stay in the workspace (et_workspace_layout).  Grouping tasks notify
- * the events of the experts their tokens selected (data-dependent targets); in dynamic
- * mode the notify that zeroes expert e's event pushes its task range
- * tasks[task_indptr[e] : task_indptr[e+1]].  Deterministic: no float atomics.
+ * the events of the experts their tokens selected (data-dependent targets); expert e's
+ * gate/up tasks tasks[task_indptr[e] : task_indptr[e+1]] wait on that event.  In
+ * dynamic mode the GEMM tasks are queued at the scan, in the order
+ * et_opts.queue_order selects (ET_QORDER_*).  Deterministic: no float atomics.
  * H and I must be multiples of 128 (checked when the workspace is planned).  The
  * tile variant follows the token count unless et_opts.tile forces one; a forced
  * variant whose column tiles do not divide H or I (the wide variants 3 and 4 cover
