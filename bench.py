@@ -403,6 +403,8 @@ def main():
     ap.add_argument("--fetch", type=int, default=2)
     ap.add_argument("--queue-order", default="auto", choices=("auto", "ready", "static"),
                     help="dynamic schedule of the MoE GEMM tasks (et_opts.queue_order)")
+    ap.add_argument("--tile", type=int, default=-1,
+                    help="MoE tile variant override (et_opts.tile; -1: chosen from the token count)")
     ap.add_argument("--no-modes", action="store_true",
                     help="time only --sched (default: every schedule, reported in config)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -460,7 +462,8 @@ def main():
     def step(sched=args.sched, order=args.queue_order):
         g, u, d = copies[turn[0] % len(copies)]
         turn[0] += 1
-        et.moe_layer(logits, x, g, u, d, out, ws, sched, fetch_batch=args.fetch, queue_order=order)
+        et.moe_layer(logits, x, g, u, d, out, ws, sched, fetch_batch=args.fetch, queue_order=order,
+                     tile=args.tile)
 
     step()
     torch.cuda.synchronize()
@@ -511,7 +514,7 @@ def main():
     # workgroup's real-time and shader-clock stamps at start and end
     g, u, d = copies[0]
     et.moe_layer(logits, x, g, u, d, out, ws, args.sched, fetch_batch=args.fetch,
-                 queue_order=args.queue_order, debug=et.DEBUG_CLOCK)
+                 queue_order=args.queue_order, tile=args.tile, debug=et.DEBUG_CLOCK)
     torch.cuda.synchronize()
     stamps = ws.clock_stamps()[: et.num_workers()].cpu().long()
     d_rt = (stamps[:, 1, 0] - stamps[:, 0, 0]) & 0xFFFFFFFF
@@ -546,7 +549,7 @@ def main():
             "fetch_batch_note": "dynamic schedule, ready order: at most this many queue slots per "
                                 "claim, and no more than the worker's share of the published slots; "
                                 "static order: one entry per claim",
-            "queue_order": args.queue_order,
+            "queue_order": args.queue_order, "tile_override": args.tile,
             "active_experts": n_active, "max_rows_per_expert": max_rows,
             "us_per_layer_mean": round(1e3 * ms, 2),
             "us_per_layer_median": round(1e3 * per_sorted[len(per) // 2], 2),
