@@ -111,3 +111,43 @@ def test_full_size_block_cover(ws, T, sched):
     assert_rel(got, ref, 1e-2, "out (%d tokens)" % len(sample))
     if T == 512:
         assert np.isfinite(out.cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("T", [2048, 8192])
+@pytest.mark.parametrize("sched", ["static", "dynamic"])
+def test_full_size_event_invariants(ws, T, sched):
+    """At the benchmark's sizes (about 12,000 and 33,000 tasks): every task
+    ran exactly once, every row block's E_h ended at its gate/up tiles (both
+    schedules: the dynamic schedule takes the static-order queue here), every
+    expert's E_exp at its routed rows (dynamic), and EV_DOWN at the number of
+    down tiles."""
+    cfg = synth.MOE_PRESETS[NAME]
+    H, I, E, k = cfg["hidden"], cfg["inter"], cfg["n_experts"], cfg["top_k"]
+    wg, wu, wd = moe_weights(NAME)
+    logits, x = synth.moe_activations(cfg, T, device=DEV)
+    out = torch.empty((T, H), device=DEV)
+    ws.runs().zero_()
+    say("moe_large invariants", T, sched)
+    et.moe_layer(logits, x, wg, wu, wd, out, ws, sched, debug=et.DEBUG_COUNTS)
+    torch.cuda.synchronize()
+    st = ws.status()
+    assert st["status"] == 0, st
+    counts = et.moe_aux(ws, T)["counts"].cpu().numpy().astype(np.int64)
+    nr = min(128, 8192 // E, -(-T // 8))
+    rows, nt1, nt2 = 128, I // 128, H // 256
+    nb = int((-(-counts // rows)).sum())
+    ccols = 1024 if -(-T // 16) * -(-H // 1024) >= 4 * et.num_workers() else 256
+    ncomb = -(-T // 16) * -(-H // ccols)
+    total = 2 * nr + 1 + nb * (nt1 + nt2) + ncomb
+    runs = ws.runs().cpu().numpy()
+    assert (runs[:total] == 1).all() and (runs[total:] == 0).all()
+    cnt = ws.counters(1 - st["bank"]).cpu().numpy()
+    ev_exp, ev_he, ev_h = 8, 8 + E, 8 + 2 * E
+    assert cnt[0] == -nr
+    assert cnt[4] == -nb * nt2
+    assert (cnt[ev_h:ev_h + nb] == -nt1).all()
+    assert (cnt[ev_he:ev_he + E] == 0).all()
+    if sched == "dynamic":
+        assert (cnt[ev_exp:ev_exp + E] == -counts).all()
+    else:
+        assert (cnt[ev_exp:ev_exp + E] == 0).all() and cnt[2] == -nr
