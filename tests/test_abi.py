@@ -61,3 +61,18 @@ def test_call_errors_enqueue_nothing():
     r = L.et_splitk_reduce(None, 64, None, None, ctypes.c_void_p(256), ctypes.byref(pm), 0,
                            None, None)
     assert r == et.EWORKSPACE
+
+
+def test_option_errors_enqueue_nothing():
+    # Out-of-range options are rejected before any HIP call: queue order,
+    # claim batch, queue shards and tile variant.
+    L = et.lib()
+    p = et.plan_workspace(et.WL_MOE, 64, 2048, 768, 128, 8)
+    fake_ws = ctypes.c_void_p(256)   # aligned, never dereferenced on the host
+    for kw in ({"queue_order": "static"}, {"fetch_batch": 9}, {"queue_shards": 3}, {"tile": 99}):
+        o = et._opts(**kw)
+        if "queue_order" in kw:
+            o.queue_order = 7
+        r = L.et_moe_layer(None, None, 8, None, None, None, None, fake_ws, ctypes.byref(p),
+                           et.SCHED_DYNAMIC, ctypes.byref(o), None)
+        assert r == et.EINVAL, (kw, r)
